@@ -1,0 +1,180 @@
+"""CPU oracle for sparse NVFP4-MLA decode -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The library in
+``sparse_mla_decode_amd`` never imports it and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, scalar loops); this
+module only builds it with gcc and marshals numpy arrays through ctypes.
+BF16 tensors travel as their uint16 bit patterns (numpy has no bfloat16).
+
+Every function here is pinned by the CPU tests in ``tests/test_oracle_*.py``
+(exhaustive format tables against PyTorch's float8_e4m3fn, brute force over
+all BF16 inputs, dense attention through a library routine, one-hot, uniform
+and single-entry closed forms, invariances, and the byte counts the pages
+print, stored under ``tests/golden/``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+ROW_BYTES = 352
+PAGE_ROWS = 64
+LATENT = 512
+DIM = 576
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (fp64, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-std=c11", "-Wall", "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i64, i32, u8, dbl = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint8, ctypes.c_double
+    lib.oracle_e4m3_value.argtypes = [u8]
+    lib.oracle_e4m3_value.restype = dbl
+    lib.oracle_e4m3_nearest.argtypes = [dbl, dbl]
+    lib.oracle_e4m3_nearest.restype = u8
+    lib.oracle_e2m1_value.argtypes = [u8]
+    lib.oracle_e2m1_value.restype = dbl
+    lib.oracle_e2m1_nearest.argtypes = [dbl, dbl]
+    lib.oracle_e2m1_nearest.restype = u8
+    lib.oracle_e4m3_value_many.argtypes = [P, i64, P]
+    lib.oracle_e4m3_value_many.restype = None
+    lib.oracle_e4m3_nearest_many.argtypes = [P, i64, dbl, P]
+    lib.oracle_e4m3_nearest_many.restype = None
+    lib.oracle_e2m1_nearest_many.argtypes = [P, P, i64, P]
+    lib.oracle_e2m1_nearest_many.restype = None
+    lib.oracle_quant_rows.argtypes = [P, i64, P]
+    lib.oracle_quant_rows.restype = None
+    lib.oracle_dequant_rows.argtypes = [P, i64, P]
+    lib.oracle_dequant_rows.restype = None
+    lib.oracle_kv_quant_append.argtypes = [P, i64, P, P, i64]
+    lib.oracle_kv_quant_append.restype = i64
+    lib.oracle_sparse_mla_decode.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, dbl,
+                                             P, P, ctypes.c_int]
+    lib.oracle_sparse_mla_decode.restype = None
+    lib.oracle_row_bytes.restype = ctypes.c_int
+    lib.oracle_page_rows.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# -- format functions, vectorised over numpy arrays ------------------------
+
+def e4m3_value(codes) -> np.ndarray:
+    """Exact value of each E4M3FN code (NaN for S.1111.111)."""
+    c = _c(codes, np.uint8)
+    out = np.zeros(c.shape, dtype=np.float64)
+    _load().oracle_e4m3_value_many(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def e4m3_nearest(num, den: float = 1.0) -> np.ndarray:
+    """Code of the E4M3 value nearest num/den (ties to even, saturating)."""
+    x = _c(num, np.float64)
+    out = np.zeros(x.shape, dtype=np.uint8)
+    _load().oracle_e4m3_nearest_many(_ptr(x), x.size, float(den), _ptr(out))
+    return out
+
+
+def e2m1_value(nibs) -> np.ndarray:
+    lib = _load()
+    nibs = np.asarray(nibs, dtype=np.uint8)
+    return np.array([lib.oracle_e2m1_value(int(c)) for c in nibs.ravel()],
+                    dtype=np.float64).reshape(nibs.shape)
+
+
+def e2m1_nearest(x, S) -> np.ndarray:
+    """Nibble nearest x / S (ties to even code, saturating, sign copied)."""
+    xx = _c(x, np.float64)
+    SS = _c(np.broadcast_to(np.asarray(S, dtype=np.float64), xx.shape), np.float64)
+    out = np.zeros(xx.shape, dtype=np.uint8)
+    _load().oracle_e2m1_nearest_many(_ptr(xx), _ptr(SS), xx.size, _ptr(out))
+    return out
+
+
+# -- rows ---------------------------------------------------------------
+
+def quant_rows(rows_bf16_bits: np.ndarray) -> np.ndarray:
+    """[n,576] uint16 (BF16 bit patterns) -> [n,352] uint8 NVFP4 rows."""
+    x = _c(rows_bf16_bits, np.uint16)
+    assert x.ndim == 2 and x.shape[1] == DIM, x.shape
+    out = np.zeros((x.shape[0], ROW_BYTES), dtype=np.uint8)
+    if x.shape[0]:
+        _load().oracle_quant_rows(_ptr(x), x.shape[0], _ptr(out))
+    return out
+
+
+def dequant_rows(rows: np.ndarray) -> np.ndarray:
+    """[n,352] uint8 -> [n,576] float64 exact values."""
+    r = _c(rows, np.uint8)
+    assert r.ndim == 2 and r.shape[1] == ROW_BYTES, r.shape
+    out = np.zeros((r.shape[0], DIM), dtype=np.float64)
+    if r.shape[0]:
+        _load().oracle_dequant_rows(_ptr(r), r.shape[0], _ptr(out))
+    return out
+
+
+def kv_quant_append(rows_bf16_bits: np.ndarray, slot_mapping: np.ndarray,
+                    cache: np.ndarray) -> int:
+    """Quantise rows into ``cache`` ([P,64,352] uint8, modified in place)."""
+    x = _c(rows_bf16_bits, np.uint16)
+    s = _c(slot_mapping, np.int32)
+    assert cache.dtype == np.uint8 and cache.flags.c_contiguous
+    assert cache.ndim == 3 and cache.shape[1:] == (PAGE_ROWS, ROW_BYTES)
+    assert x.shape == (s.shape[0], DIM)
+    return int(_load().oracle_kv_quant_append(_ptr(x), x.shape[0], _ptr(s), _ptr(cache),
+                                              cache.shape[0]))
+
+
+def sparse_mla_decode(q_bf16_bits: np.ndarray, cache: np.ndarray, page_table: np.ndarray,
+                      seq_lens: np.ndarray, topk: np.ndarray, softmax_scale: float,
+                      nthreads: int = 0):
+    """Returns (out [B,H,512] float64, lse [B,H] float64)."""
+    q = _c(q_bf16_bits, np.uint16)
+    c = _c(cache, np.uint8)
+    pt = _c(page_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    tk = _c(topk, np.int32)
+    B, H, D = q.shape
+    assert D == DIM and c.ndim == 3 and c.shape[1:] == (PAGE_ROWS, ROW_BYTES)
+    assert pt.ndim == 2 and pt.shape[0] == B and sl.shape == (B,)
+    assert tk.ndim == 2 and tk.shape[0] == B
+    out = np.zeros((B, H, LATENT), dtype=np.float64)
+    lse = np.zeros((B, H), dtype=np.float64)
+    _load().oracle_sparse_mla_decode(_ptr(q), _ptr(c), c.shape[0], _ptr(pt), pt.shape[1],
+                                     _ptr(sl), _ptr(tk), B, H, tk.shape[1],
+                                     float(softmax_scale), _ptr(out), _ptr(lse), int(nthreads))
+    return out, lse
