@@ -1,0 +1,159 @@
+/*
+ * smla.h -- C ABI of the MI355X (gfx950) sparse NVFP4-MLA decode library.
+ *
+ * Two operations make up the decode-side hot path of sparse multi-head latent
+ * attention over a paged, NVFP4-compressed latent KV cache:
+ *
+ *   smla_kv_quant_append   BF16 KV rows -> 352-byte NVFP4 rows in the paged cache
+ *   smla_sparse_mla_decode q, cache, page table, top-k indices -> out, lse
+ *
+ * Sources (page titles; no other document is needed to read this header):
+ *   [P1] "Prime Inference: serving GLM-5.3 to agents is a KV-cache problem",
+ *        section "Four bits per latent value: where 352 comes from" (row bytes:
+ *        512 latent values at 4 bits = 256 B, one FP8 scale per 16 values =
+ *        32 B, 64 rope values in FP8 = 64 B) and section "A kernel that reads
+ *        four bits directly" (selected rows are unpacked on chip; -1 entries of
+ *        short contexts carry no data).
+ *   [P3] Prime Intellect's "Prime Inference" launch post, the paragraphs on the
+ *        NVFP4 latent and on the native sparse-MLA kernel (FP16 operands,
+ *        FP32 accumulation, no intermediate buffer in GPU memory).
+ *   [P5] "GLM-5.3 PCP/DCP long-context on H200", section 1 (every selected KV
+ *        row serves all heads of the absorbed query).
+ *
+ * Row format (one token, 352 bytes; readings where the pages are silent):
+ *   bytes [0,256)   latent values 0..511 as e2m1 nibbles, value 2i in the low
+ *                   nibble of byte i, value 2i+1 in the high nibble;
+ *   bytes [256,288) one OCP FP8 E4M3 (E4M3FN) scale per block of 16 latent
+ *                   values, in block order; scale = E4M3 value nearest
+ *                   amax(|block|)/6 (ties to even); nibble = e2m1 value
+ *                   nearest x/scale (ties to the even code, saturating at 6,
+ *                   0 when the scale is 0); the input's sign bit is copied;
+ *   bytes [288,352) the 64 rope values as OCP FP8 E4M3 (nearest, ties to
+ *                   even, saturating at +-448), no scale.
+ * A page holds 64 consecutive rows (22,528 bytes); the cache is
+ * [num_pages][64][352] bytes.  Token t of sequence b lives in physical page
+ * page_table[b][t / 64], row t % 64.
+ *
+ * Conventions for every entry point:
+ *   - All pointers are DEVICE pointers on the current HIP device, except that
+ *     `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - The caller owns every buffer.  The library allocates nothing, frees
+ *     nothing and keeps no pointer after a call returns.
+ *   - Work is enqueued asynchronously on `stream`; nothing is synchronised.
+ *   - Arguments are validated on the host before anything is launched.  On
+ *     any error the call returns a negative SMLA_ERR_* code and no buffer is
+ *     touched.  smla_strerror() names the code.
+ *   - Device-resident data (indices, slots, page ids, sequence lengths) is
+ *     never trusted: an entry outside its valid range is skipped, never
+ *     dereferenced.
+ *   - Inputs (rows, q) must be finite.  q must also lie inside the FP16 range
+ *     (|q| < 65504), because the score contraction runs on FP16 operands.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMLA_LATENT 512
+#define SMLA_ROPE 64
+#define SMLA_DIM 576
+#define SMLA_ROW_BYTES 352
+#define SMLA_PAGE_ROWS 64
+#define SMLA_PAGE_BYTES (SMLA_PAGE_ROWS * SMLA_ROW_BYTES)
+#define SMLA_MAX_TOPK 2048
+
+enum {
+    SMLA_OK = 0,
+    SMLA_ERR_NULL = -1,        /* a required pointer is NULL                  */
+    SMLA_ERR_SHAPE = -2,       /* a size is out of range                       */
+    SMLA_ERR_UNSUPPORTED = -3, /* a supported-but-not-built configuration      */
+    SMLA_ERR_ALIGN = -4,       /* a pointer is not aligned as documented       */
+    SMLA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required   */
+    SMLA_ERR_LAUNCH = -6,      /* the HIP runtime rejected a kernel launch     */
+    SMLA_ERR_DEVICE = -7       /* no usable gfx950 device is current           */
+};
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *smla_strerror(int code);
+
+/* Library ABI version (major * 100 + minor). */
+int smla_version(void);
+
+/*
+ * Quantise n BF16 rows into the paged NVFP4 cache [P1 row-bytes table; P3].
+ *
+ *   rows_bf16     [n][576] BF16 (latent 0..511, then rope 0..63), 16-byte aligned
+ *   n             number of rows, 0 <= n <= 2^31-1 (n == 0 enqueues nothing)
+ *   slot_mapping  [n] int32; row i is written to slot s = slot_mapping[i],
+ *                 i.e. cache page s / 64, row s % 64.  A slot < 0 (e.g. -1)
+ *                 or >= num_pages*64 is skipped.  Two rows naming the same
+ *                 slot in one call: which one lands is unspecified.
+ *   cache         [num_pages][64][352] uint8, 256-byte aligned
+ *   num_pages     1 <= num_pages <= 2^25
+ *
+ * The packed bytes equal, bit for bit, the format rules stated at the top.
+ */
+int smla_kv_quant_append(const void *rows_bf16, int64_t n, const int32_t *slot_mapping,
+                         uint8_t *cache, int64_t num_pages, void *stream);
+
+/*
+ * Bytes of device workspace smla_sparse_mla_decode needs for this shape
+ * (0 means none).  The first 512 KiB of a workspace hold ticket counters
+ * (one per sequence and head group) at fixed offsets; the rest holds
+ * per-split partial results.  The workspace must be zero-filled before its
+ * first use; every call leaves the counters at zero again, so one zeroed
+ * buffer can be reused by any number of calls of any shape on one stream.
+ * Calls that overlap in time must not share a workspace.
+ */
+size_t smla_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t topk);
+
+/*
+ * Sparse MLA decode over the NVFP4 cache [P1 kernel section; P3 native
+ * kernel paragraph; P5 section 1].  For each sequence b and head h, over the
+ * usable entries t of topk_indices[b] (list order, repeats counted):
+ *
+ *     k_t      = the 576 values of row t decoded exactly from the cache
+ *     s_t      = softmax_scale * sum_{d<576} q[b,h,d] * k_t[d]
+ *     out[b,h] = sum_t exp(s_t) k_t[0:512] / sum_t exp(s_t)
+ *     lse[b,h] = ln sum_t exp(s_t)            (natural log, scale included)
+ *
+ * An entry t is usable iff 0 <= t < seq_lens[b], t/64 < max_pages and
+ * 0 <= page_table[b][t/64] < num_pages; all others (the -1 padding of short
+ * contexts among them) are skipped and cost no cache read.  With no usable
+ * entry, out[b,h,:] = 0 and lse[b,h] = -inf.
+ *
+ *   q_bf16        [batch][heads][576] BF16, 16-byte aligned
+ *   cache         [num_pages][64][352] uint8, 256-byte aligned, 1 <= num_pages <= 2^25
+ *   page_table    [batch][max_pages] int32, max_pages >= 1
+ *   seq_lens      [batch] int32
+ *   topk_indices  [batch][topk] int32
+ *   batch         1 <= batch <= 65535
+ *   heads         16 or 64
+ *   topk          1 <= topk <= 2048
+ *   out           [batch][heads][512] fp32, 16-byte aligned (written)
+ *   lse           [batch][heads] fp32 (written)
+ *   workspace     >= smla_decode_workspace_bytes(batch, heads, topk) bytes,
+ *                 256-byte aligned, zero-filled before first use (may be NULL
+ *                 when that size is 0)
+ *
+ * Scores use FP16 operands (q and the decoded values; the decoded values are
+ * exact in FP16) with FP32 accumulation; softmax weights are rounded to FP16
+ * for the value contraction; the sums run in FP32.
+ */
+int smla_sparse_mla_decode(const void *q_bf16, const uint8_t *cache, int64_t num_pages,
+                           const int32_t *page_table, int32_t max_pages,
+                           const int32_t *seq_lens, const int32_t *topk_indices,
+                           int32_t batch, int32_t heads, int32_t topk, float softmax_scale,
+                           float *out, float *lse, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H */

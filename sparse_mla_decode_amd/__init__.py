@@ -1,0 +1,177 @@
+"""Sparse NVFP4-MLA decode on MI355X (gfx950): Python binding of libsmla.so.
+
+This module is argument marshalling only.  Every step of the path runs in the
+HIP kernels behind the C ABI in ``include/smla.h``; PyTorch provides device
+memory and the current stream.  There is no fallback: if ``libsmla.so`` has
+not been built, importing this package raises.
+
+    kv_quant_append(rows, slot_mapping, cache)
+        rows [n,576] bf16, slot_mapping [n] int32, cache [P,64,352] uint8 (in place)
+    sparse_mla_decode(q, cache, page_table, seq_lens, topk, softmax_scale)
+        -> (out [B,H,512] fp32, lse [B,H] fp32)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsmla.so")
+
+LATENT = 512
+ROPE = 64
+DIM = 576
+ROW_BYTES = 352
+PAGE_ROWS = 64
+MAX_TOPK = 2048
+
+ERRORS = {
+    0: "SMLA_OK", -1: "SMLA_ERR_NULL", -2: "SMLA_ERR_SHAPE", -3: "SMLA_ERR_UNSUPPORTED",
+    -4: "SMLA_ERR_ALIGN", -5: "SMLA_ERR_WORKSPACE", -6: "SMLA_ERR_LAUNCH", -7: "SMLA_ERR_DEVICE",
+}
+
+# exported symbols, in the order include/smla.h declares them
+EXPORTS = ("smla_strerror", "smla_version", "smla_kv_quant_append",
+           "smla_decode_workspace_bytes", "smla_sparse_mla_decode")
+
+
+class SmlaError(RuntimeError):
+    def __init__(self, code: int, lib):
+        msg = lib.smla_strerror(code).decode()
+        super().__init__("%s (%d): %s" % (ERRORS.get(code, "?"), code, msg))
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libsmla.so is not built (expected %s); run `python -c \"import "
+            "__graft_entry__ as g; g.build()\"` or `python sparse_mla_decode_amd/build.py`"
+            % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                            ctypes.c_size_t)
+    lib.smla_strerror.argtypes = [ctypes.c_int]
+    lib.smla_strerror.restype = ctypes.c_char_p
+    lib.smla_version.argtypes = []
+    lib.smla_version.restype = ctypes.c_int
+    lib.smla_kv_quant_append.argtypes = [P, i64, P, P, i64, P]
+    lib.smla_kv_quant_append.restype = ctypes.c_int
+    lib.smla_decode_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.smla_decode_workspace_bytes.restype = sz
+    lib.smla_sparse_mla_decode.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, f32,
+                                           P, P, P, sz, P]
+    lib.smla_sparse_mla_decode.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+_ws_lock = threading.Lock()
+_workspaces: dict = {}
+
+
+def _check(code: int):
+    if code != 0:
+        raise SmlaError(code, lib)
+
+
+def _stream_ptr(device: torch.device, stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def _req(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_cuda:
+        raise ValueError("%s must be on a GPU" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def version() -> int:
+    return int(lib.smla_version())
+
+
+def decode_workspace_bytes(batch: int, heads: int, topk: int) -> int:
+    return int(lib.smla_decode_workspace_bytes(batch, heads, topk))
+
+
+def workspace_for(device: torch.device, nbytes: int, stream=None) -> torch.Tensor:
+    """A zero-initialised workspace of at least nbytes, cached per (device, stream).
+
+    The decode kernels leave the workspace's counters at zero after every call,
+    so the buffer is zeroed only when it is first allocated."""
+    key = (device.index, _stream_ptr(device, stream))
+    with _ws_lock:
+        ws = _workspaces.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            _workspaces[key] = ws
+        return ws
+
+
+def kv_quant_append(rows: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tensor,
+                    stream=None) -> None:
+    """Quantise BF16 rows [n,576] into cache slots (page*64 + row) of cache [P,64,352]."""
+    _req(cache, "cache", torch.uint8, 3)
+    dev = cache.device
+    _req(rows, "rows", torch.bfloat16, 2, dev)
+    _req(slot_mapping, "slot_mapping", torch.int32, 1, dev)
+    if rows.shape[1] != DIM or slot_mapping.shape[0] != rows.shape[0]:
+        raise ValueError("rows must be [n,576] and slot_mapping [n]")
+    if tuple(cache.shape[1:]) != (PAGE_ROWS, ROW_BYTES):
+        raise ValueError("cache must be [num_pages,64,352]")
+    _check(lib.smla_kv_quant_append(rows.data_ptr(), rows.shape[0], slot_mapping.data_ptr(),
+                                    cache.data_ptr(), cache.shape[0], _stream_ptr(dev, stream)))
+
+
+def sparse_mla_decode(q: torch.Tensor, cache: torch.Tensor, page_table: torch.Tensor,
+                      seq_lens: torch.Tensor, topk: torch.Tensor, softmax_scale: float,
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None):
+    """Sparse MLA decode; returns (out [B,H,512] fp32, lse [B,H] fp32)."""
+    _req(cache, "cache", torch.uint8, 3)
+    dev = cache.device
+    _req(q, "q", torch.bfloat16, 3, dev)
+    _req(page_table, "page_table", torch.int32, 2, dev)
+    _req(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _req(topk, "topk", torch.int32, 2, dev)
+    B, H, D = q.shape
+    if D != DIM:
+        raise ValueError("q must be [B,H,576]")
+    if tuple(cache.shape[1:]) != (PAGE_ROWS, ROW_BYTES):
+        raise ValueError("cache must be [num_pages,64,352]")
+    if page_table.shape[0] != B or seq_lens.shape[0] != B or topk.shape[0] != B:
+        raise ValueError("page_table, seq_lens and topk need one row per sequence")
+    K = topk.shape[1]
+    if out is None:
+        out = torch.empty((B, H, LATENT), dtype=torch.float32, device=dev)
+    else:
+        _req(out, "out", torch.float32, 3, dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    else:
+        _req(lse, "lse", torch.float32, 2, dev)
+    need = decode_workspace_bytes(B, H, K)
+    if workspace is None and need > 0:
+        workspace = workspace_for(dev, need, stream)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.smla_sparse_mla_decode(
+        q.data_ptr(), cache.data_ptr(), cache.shape[0], page_table.data_ptr(),
+        page_table.shape[1], seq_lens.data_ptr(), topk.data_ptr(), B, H, K,
+        float(softmax_scale), out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes,
+        _stream_ptr(dev, stream)))
+    return out, lse

@@ -1,0 +1,142 @@
+// kv_quant_append: BF16 KV rows -> 352-byte NVFP4 rows in the paged cache.
+//
+// Format: "Prime Inference: serving GLM-5.3 to agents is a KV-cache problem",
+// section "Four bits per latent value: where 352 comes from" -- the 512 latent
+// values as e2m1 nibbles with one FP8 E4M3 scale per 16, the 64 rope values
+// as FP8.  The rounding rules (scale = E4M3 nearest amax/6, nibble = e2m1
+// nearest x/scale, ties to even, sign copied) are the readings stated in
+// include/smla.h; every decision below is taken with exact fp32 operations so
+// the bytes are reproducible bit for bit.
+//
+// Mapping: 32 lanes per row, lane j owns latent block j (16 values) and rope
+// values 2j, 2j+1.  A 256-thread workgroup quantises 8 rows.  The kernel is
+// HBM-bound (1152 B read and 352 B written per row); loads of a row are one
+// contiguous 1 KiB sweep across its 32 lanes.
+#include "smla_internal.h"
+
+namespace smla {
+namespace {
+
+// Magnitude of an E4M3 code's low 7 bits: (1 + m/8) 2^(e-7), or m 2^-9 when e = 0.
+__device__ __forceinline__ float e4m3_mag(uint32_t c) {
+    uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    float mant = e ? (float)(8u + m) : (float)(2u * m);  // e==0: m/8 * 2^-6 = 2m * 2^-10
+    int ex = e ? (int)e - 10 : -10;
+    return ldexpf(mant, ex);
+}
+
+// E4M3 code (sign copied) of the value nearest v, ties to even, saturating.
+__device__ __forceinline__ uint32_t e4m3_nearest(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    float a = __uint_as_float(u & 0x7FFFFFFFu);
+    uint32_t code;
+    if (a > 448.0f) {
+        code = 0x7E;                          // past 448 only 448 is finite
+    } else if (a <= 0x1p-10f) {
+        code = 0;                             // half the smallest subnormal: ties to 0
+    } else if (a < 0x1p-6f) {
+        code = (uint32_t)rintf(a * 512.0f);   // subnormal grid m 2^-9; 8 -> 0x08 = 2^-6
+    } else {
+        int E = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;   // a is a normal fp32
+        uint32_t m = (uint32_t)rintf(ldexpf(a, 3 - E));           // in [8, 16]
+        if (m == 16u) { E += 1; m = 8u; }
+        code = ((uint32_t)(E + 7) << 3) | (m - 8u);
+    }
+    return sign | code;
+}
+
+// Scale code: E4M3 value nearest amax / 6, ties to even.  The fp32 quotient
+// gives a first guess; exact comparisons of amax with 6 * midpoint (a
+// midpoint has at most 5 significant bits, so 3 * (lo + hi) is exact) settle
+// it, including exact ties.
+__device__ __forceinline__ uint32_t scale_code(float amax) {
+    uint32_t s = e4m3_nearest(amax * (1.0f / 6.0f)) & 0x7Fu;
+    for (int it = 0; it < 3; ++it) {
+        if (s < 0x7Eu) {
+            float mid6 = 3.0f * (e4m3_mag(s) + e4m3_mag(s + 1));
+            if (amax > mid6 || (amax == mid6 && ((s + 1) & 1u) == 0)) { ++s; continue; }
+        }
+        if (s > 0u) {
+            float mid6 = 3.0f * (e4m3_mag(s - 1) + e4m3_mag(s));
+            if (amax < mid6 || (amax == mid6 && ((s - 1) & 1u) == 0)) { --s; continue; }
+        }
+        break;
+    }
+    return s;
+}
+
+// e2m1 magnitude code of a / S: count of midpoints passed.  The midpoints
+// 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 (times S, exact) alternate between
+// ties-down (even code below) and ties-up (even code above).
+__device__ __forceinline__ uint32_t e2m1_code(float a, const float t[7]) {
+    uint32_t c = 0;
+    c += a > t[0];
+    c += a >= t[1];
+    c += a > t[2];
+    c += a >= t[3];
+    c += a > t[4];
+    c += a >= t[5];
+    c += a > t[6];
+    return c;
+}
+
+__device__ __forceinline__ float bf16_abs(uint32_t h) { return __uint_as_float((h & 0x7FFFu) << 16); }
+
+__global__ __launch_bounds__(256) void kv_quant_append_kernel(const uint16_t *__restrict__ rows,
+                                                              int64_t n,
+                                                              const int32_t *__restrict__ slots,
+                                                              uint8_t *__restrict__ cache,
+                                                              int64_t num_slots) {
+    const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+    const int j = threadIdx.x & 31;
+    if (row >= n) return;
+    const int64_t slot = slots[row];
+    if (slot < 0 || slot >= num_slots) return;
+    const uint16_t *x = rows + row * kDim;
+    uint8_t *dst = cache + slot * kRowBytes;
+
+    // ---- latent block j ----
+    const uint4 lo = *reinterpret_cast<const uint4 *>(x + j * kBlock);
+    const uint4 hi = *reinterpret_cast<const uint4 *>(x + j * kBlock + 8);
+    uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    uint32_t amax_bits = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        amax_bits = max(amax_bits, w[i] & 0x7FFFu);
+        amax_bits = max(amax_bits, (w[i] >> 16) & 0x7FFFu);
+    }
+    const float amax = __uint_as_float(amax_bits << 16);
+    const uint32_t s = scale_code(amax);
+    const float S = e4m3_mag(s);
+    const float t[7] = {0.25f * S, 0.75f * S, 1.25f * S, 1.75f * S, 2.5f * S, 3.5f * S, 5.0f * S};
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+        const uint32_t mag = (S == 0.0f) ? 0u : e2m1_code(bf16_abs(h), t);
+        const uint32_t nib = mag | ((h >> 12) & 8u);
+        packed[i >> 3] |= nib << ((i & 7) * 4);
+    }
+    *reinterpret_cast<uint2 *>(dst + j * 8) = make_uint2(packed[0], packed[1]);
+    dst[kScaleOff + j] = (uint8_t)s;
+
+    // ---- rope values 2j, 2j+1 ----
+    const uint32_t r = *reinterpret_cast<const uint32_t *>(x + kLatent + 2 * j);
+    const uint32_t c0 = e4m3_nearest(__uint_as_float((r & 0xFFFFu) << 16));
+    const uint32_t c1 = e4m3_nearest(__uint_as_float(r & 0xFFFF0000u));
+    *reinterpret_cast<uint16_t *>(dst + kRopeOff + 2 * j) = (uint16_t)(c0 | (c1 << 8));
+}
+
+}  // namespace
+
+hipError_t launch_kv_quant_append(const uint16_t *rows, int64_t n, const int32_t *slots,
+                                  uint8_t *cache, int64_t num_pages, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 7) / 8;
+    hipLaunchKernelGGL(kv_quant_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, rows,
+                       n, slots, cache, num_pages * kPageRows);
+    return hipGetLastError();
+}
+
+}  // namespace smla

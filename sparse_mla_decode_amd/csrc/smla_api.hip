@@ -1,0 +1,100 @@
+// Host side of the C ABI declared in include/smla.h: argument validation
+// (everything is checked before anything is launched) and dispatch.
+#include "smla.h"
+#include "smla_internal.h"
+
+#include <string.h>
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SMLA_ERR_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SMLA_ERR_DEVICE;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return SMLA_ERR_DEVICE;
+    return SMLA_OK;
+}
+
+// Cached per process: the library only runs on gfx950 and the answer cannot change.
+int device_ok() {
+    static int cached = 1;  // 1 = not yet asked
+    if (cached == 1) cached = check_device();
+    return cached;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *smla_strerror(int code) {
+    switch (code) {
+        case SMLA_OK: return "ok";
+        case SMLA_ERR_NULL: return "a required pointer is NULL";
+        case SMLA_ERR_SHAPE: return "a size argument is out of range";
+        case SMLA_ERR_UNSUPPORTED: return "unsupported configuration (heads must be 16 or 64)";
+        case SMLA_ERR_ALIGN: return "a pointer is not aligned as required";
+        case SMLA_ERR_WORKSPACE: return "workspace missing or too small";
+        case SMLA_ERR_LAUNCH: return "kernel launch failed";
+        case SMLA_ERR_DEVICE: return "no gfx950 device is current";
+        default: return "unknown status code";
+    }
+}
+
+int smla_version(void) { return 100; }
+
+int smla_kv_quant_append(const void *rows_bf16, int64_t n, const int32_t *slot_mapping,
+                         uint8_t *cache, int64_t num_pages, void *stream) {
+    if (n < 0 || n > INT32_MAX) return SMLA_ERR_SHAPE;
+    if (num_pages < 1 || num_pages > ((int64_t)1 << 25)) return SMLA_ERR_SHAPE;
+    if (n == 0) return SMLA_OK;
+    if (!rows_bf16 || !slot_mapping || !cache) return SMLA_ERR_NULL;
+    if (!aligned(rows_bf16, 16) || !aligned(cache, 256) || !aligned(slot_mapping, 4))
+        return SMLA_ERR_ALIGN;
+    const int dev = device_ok();
+    if (dev != SMLA_OK) return dev;
+    const hipError_t e = smla::launch_kv_quant_append(
+        static_cast<const uint16_t *>(rows_bf16), n, slot_mapping, cache, num_pages,
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+size_t smla_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t topk) {
+    if (batch < 1 || batch > 65535 || (heads != 16 && heads != 64) || topk < 1 ||
+        topk > SMLA_MAX_TOPK)
+        return 0;
+    return smla::plan_decode(batch, heads, topk).workspace_bytes;
+}
+
+int smla_sparse_mla_decode(const void *q_bf16, const uint8_t *cache, int64_t num_pages,
+                           const int32_t *page_table, int32_t max_pages,
+                           const int32_t *seq_lens, const int32_t *topk_indices,
+                           int32_t batch, int32_t heads, int32_t topk, float softmax_scale,
+                           float *out, float *lse, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    if (heads != 16 && heads != 64) return SMLA_ERR_UNSUPPORTED;
+    if (batch < 1 || batch > 65535 || topk < 1 || topk > SMLA_MAX_TOPK || max_pages < 1 ||
+        num_pages < 1 || num_pages > ((int64_t)1 << 25))
+        return SMLA_ERR_SHAPE;
+    if (!q_bf16 || !cache || !page_table || !seq_lens || !topk_indices || !out || !lse)
+        return SMLA_ERR_NULL;
+    if (!aligned(q_bf16, 16) || !aligned(out, 16) || !aligned(cache, 256) || !aligned(lse, 4) ||
+        !aligned(page_table, 4) || !aligned(seq_lens, 4) || !aligned(topk_indices, 4))
+        return SMLA_ERR_ALIGN;
+    const smla::DecodePlan plan = smla::plan_decode(batch, heads, topk);
+    if (plan.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.workspace_bytes) return SMLA_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return SMLA_ERR_ALIGN;
+    }
+    const int dev = device_ok();
+    if (dev != SMLA_OK) return dev;
+    const hipError_t e = smla::launch_sparse_mla_decode(
+        static_cast<const uint16_t *>(q_bf16), cache, num_pages, page_table, max_pages, seq_lens,
+        topk_indices, batch, heads, topk, softmax_scale, out, lse, workspace, plan,
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+}  // extern "C"

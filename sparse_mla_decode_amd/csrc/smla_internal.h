@@ -1,0 +1,51 @@
+// Internal declarations shared by the library's translation units.
+// Format constants follow the row layout of "Prime Inference: serving GLM-5.3
+// to agents is a KV-cache problem", section "Four bits per latent value: where
+// 352 comes from": 256 B of e2m1 nibbles, 32 E4M3 block scales, 64 E4M3 rope
+// bytes per 576-value row.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace smla {
+
+constexpr int kLatent = 512;
+constexpr int kRope = 64;
+constexpr int kDim = kLatent + kRope;
+constexpr int kBlock = 16;                   // latent values per scale
+constexpr int kScaleOff = kLatent / 2;       // 256
+constexpr int kRopeOff = kScaleOff + kLatent / kBlock;  // 288
+constexpr int kRowBytes = kRopeOff + kRope;  // 352
+constexpr int kPageRows = 64;
+constexpr int kMaxTopk = 2048;
+constexpr int kMaxBatch = 65535;
+// Decode workspace: one int32 ticket counter per (sequence, head group) at a
+// fixed offset (sized for the largest batch and two head groups), then the
+// per-split partial results.
+constexpr size_t kCounterBytes = (size_t)131072 * sizeof(int32_t);
+
+// Decode launch plan shared by the host entry points and the kernel.
+struct DecodePlan {
+    int heads_per_group;  // 16 or 32: heads one workgroup serves from each row
+    int groups;           // heads / heads_per_group
+    int splits;           // workgroups sharing one (sequence, head group)
+    int per_split;        // top-k entries each split scans
+    size_t partial_floats;  // floats per partial result
+    size_t workspace_bytes;
+};
+
+DecodePlan plan_decode(int batch, int heads, int topk);
+
+hipError_t launch_kv_quant_append(const uint16_t *rows, int64_t n, const int32_t *slots,
+                                  uint8_t *cache, int64_t num_pages, hipStream_t stream);
+
+hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int64_t num_pages,
+                                    const int32_t *page_table, int32_t max_pages,
+                                    const int32_t *seq_lens, const int32_t *topk_idx,
+                                    int32_t batch, int32_t heads, int32_t topk, float scale,
+                                    float *out, float *lse, void *workspace,
+                                    const DecodePlan &plan, hipStream_t stream);
+
+}  // namespace smla

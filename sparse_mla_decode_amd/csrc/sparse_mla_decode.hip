@@ -1,0 +1,473 @@
+// sparse_mla_decode: absorbed-query MLA attention over the top-k selected
+// rows of a paged NVFP4 cache, dequantised on chip.
+//
+// What it computes: "Prime Inference: serving GLM-5.3 to agents is a
+// KV-cache problem", section "A kernel that reads four bits directly" (load
+// the selected 352-byte rows, unpack on chip, score, softmax and blend; -1
+// entries carry no data) and Prime Intellect's launch post, native-kernel
+// paragraph (FP16 operands, FP32 accumulation, partial results of the blocks
+// sharing a query merged in the same launch).  Every selected row serves all
+// heads of the query: "GLM-5.3 PCP/DCP long-context on H200", section 1.
+//
+// Work decomposition (gfx950: 256 CUs in 8 XCDs, 64-wide waves, 160 KB LDS):
+//   * one 256-thread workgroup (4 waves) per (sequence, head group, split);
+//     a head group is 16 or 32 heads, a split a slice of the top-k list;
+//   * prologue: the split's entries are validated, translated through the
+//     page table and compacted into LDS, so -1 padding and out-of-range
+//     entries cost neither a load nor a matrix instruction;
+//   * per tile of 64 selected rows: the raw 22.5 KB are gathered with
+//     coalesced 16-byte loads (prefetched one tile ahead) into LDS; each wave
+//     takes 16 rows, unpacks them in registers straight into the B-operand
+//     layout of v_mfma_f32_16x16x32_f16 (e2m1 -> f16 by the hardware
+//     converter, times the block scale with a packed f16 multiply; both
+//     exact), scores them against the query held in registers, and stores
+//     the unpacked latent part to LDS once; the online softmax (max and sum
+//     by lane shuffles, per-wave maxima exchanged through LDS) turns scores
+//     into f16 weights; each wave then accumulates the value contraction for
+//     its 128 of the 512 output columns, reading weights and values from LDS
+//     (values through the transposing ds_read_b64_tr_b16);
+//   * splits of one (sequence, head group) are dispatched to the same XCD;
+//     each writes its partial (m, l, O) and the last to arrive (an atomic
+//     ticket) merges them in the same launch.
+#include "smla_internal.h"
+
+namespace smla {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4_t;
+
+constexpr int kThreads = 256;
+constexpr int kTile = 64;                     // selected rows per tile (16 per wave)
+constexpr int kPieces = kTile * kRowBytes / 16;  // 16-byte pieces per tile (1408)
+constexpr int kPiecesPerThread = (kPieces + kThreads - 1) / kThreads;  // 6
+constexpr int kVStride = kLatent + 16;        // f16 elements per LDS value row (1056 B)
+constexpr int kPStride = kTile + 8;           // f16 elements per LDS weight row (144 B)
+constexpr int kKSteps = kDim / 32;            // 18 contraction steps of 32 for the scores
+
+__device__ __forceinline__ half8_t join(half2_t a, half2_t b, half2_t c, half2_t d) {
+    half8_t r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+}
+
+__device__ __forceinline__ _Float16 bf16_to_f16(uint32_t h) {
+    return (_Float16)__uint_as_float(h << 16);
+}
+
+template <int HG>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ cache,
+                              int64_t num_pages, const int32_t *__restrict__ page_table,
+                              int32_t max_pages, const int32_t *__restrict__ seq_lens,
+                              const int32_t *__restrict__ topk_idx, int32_t heads, int32_t topk,
+                              float scale_log2, float *__restrict__ out, float *__restrict__ lse,
+                              float *__restrict__ ws_partials, int32_t *__restrict__ ws_counters,
+                              int32_t units, int32_t groups, int32_t splits, int32_t per_split) {
+    constexpr int MB = HG / 16;  // 16-head MFMA row blocks
+    __shared__ __attribute__((aligned(16))) uint8_t raw_lds[kTile * kRowBytes];
+    __shared__ __attribute__((aligned(16))) _Float16 v_lds[kTile * kVStride];
+    __shared__ __attribute__((aligned(16))) _Float16 p_lds[HG * kPStride];
+    __shared__ uint32_t rowid_lds[kMaxTopk];
+    __shared__ float wmax_lds[4][HG];
+    __shared__ float lsum_lds[4][HG];
+    __shared__ int32_t scan_lds[4];
+    __shared__ int32_t flag_lds;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int n = lane & 15;   // row (scores) / column (values) within a 16-block
+    const int g = lane >> 4;   // 8-element k group
+
+    // ---- which (sequence, head group, split) ----
+    const int id = blockIdx.x;
+    const int xcd = id & 7;
+    const int rest = id >> 3;
+    const int split = rest % splits;
+    const int unit = (rest / splits) * 8 + xcd;
+    if (unit >= units) return;
+    const int b = unit / groups;
+    const int hg = unit % groups;
+    const int e_begin = split * per_split;
+    const int e_end = min(topk, e_begin + per_split);
+
+    // ---- prologue: validate, translate, compact the split's entries ----
+    const int64_t L = seq_lens[b];
+    const int64_t slots_total = num_pages * kPageRows;
+    const int per_thread = (per_split + kThreads - 1) / kThreads;
+    uint32_t rid[8];
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        rid[i] = 0xFFFFFFFFu;
+        const int e = e_begin + tid * per_thread + i;
+        if (i < per_thread && e < e_end) {
+            const int64_t t = topk_idx[(int64_t)b * topk + e];
+            if (t >= 0 && t < L && (t >> 6) < max_pages) {
+                const int64_t page = page_table[(int64_t)b * max_pages + (t >> 6)];
+                if (page >= 0 && page < num_pages) {
+                    const int64_t slot = page * kPageRows + (t & 63);
+                    if (slot < slots_total) rid[i] = (uint32_t)slot;
+                }
+            }
+        }
+        cnt += rid[i] != 0xFFFFFFFFu;
+    }
+    // exclusive scan of cnt over the workgroup (list order preserved)
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+    }
+    if (lane == 63) scan_lds[wave] = incl;
+    __syncthreads();
+    int before = 0, n_valid = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int s = scan_lds[w];
+        before += (w < wave) ? s : 0;
+        n_valid += s;
+    }
+    int pos = before + incl - cnt;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (rid[i] != 0xFFFFFFFFu) rowid_lds[pos++] = rid[i];
+
+    // ---- query for this head group, resident in registers as f16 A operands ----
+    // A[m = head][k = 8g + i] at score step j holds dim 128g + 8j + i (latent,
+    // j < 16) or 512 + 16g + 8(j-16) + i (rope): the same permutation of the
+    // 576 dims that the unpacked rows use below.
+    half8_t qa[MB][kKSteps];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int head = hg * HG + mb * 16 + n;
+        const uint16_t *qrow = q + ((int64_t)b * heads + head) * kDim;
+#pragma unroll
+        for (int j = 0; j < kKSteps; ++j) {
+            const int d0 = (j < 16) ? (128 * g + 8 * j) : (512 + 16 * g + 8 * (j - 16));
+            const uint4 v = *reinterpret_cast<const uint4 *>(qrow + d0);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qa[mb][j][2 * i] = bf16_to_f16(w4[i] & 0xFFFFu);
+                qa[mb][j][2 * i + 1] = bf16_to_f16(w4[i] >> 16);
+            }
+        }
+    }
+    __syncthreads();  // rowid_lds complete
+
+    const int n_tiles = (n_valid + kTile - 1) / kTile;
+
+    float4_t o[MB][8];
+    float m_run[MB][4], l_run[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) o[mb][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { m_run[mb][r] = -INFINITY; l_run[mb][r] = 0.f; }
+    }
+
+    // gather of one tile's raw rows: piece p = tid + 256 i is 16 bytes of row p / 22
+    uint4 pre[kPiecesPerThread];
+    auto gather = [&](int tile) {
+#pragma unroll
+        for (int i = 0; i < kPiecesPerThread; ++i) {
+            const int p = tid + kThreads * i;
+            const int r = p / 22;
+            const int c = p - r * 22;
+            const int idx = tile * kTile + r;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (p < kPieces && idx < n_valid) {
+                const uint8_t *src = cache + (int64_t)rowid_lds[idx] * kRowBytes + c * 16;
+                v = *reinterpret_cast<const uint4 *>(src);
+            }
+            pre[i] = v;
+        }
+    };
+    if (n_tiles > 0) gather(0);
+
+    for (int tile = 0; tile < n_tiles; ++tile) {
+        // (1) publish this tile's raw rows
+#pragma unroll
+        for (int i = 0; i < kPiecesPerThread; ++i) {
+            const int p = tid + kThreads * i;
+            if (p < kPieces) *reinterpret_cast<uint4 *>(raw_lds + p * 16) = pre[i];
+        }
+        __syncthreads();
+        // (2) prefetch the next tile
+        if (tile + 1 < n_tiles) gather(tile + 1);
+
+        // (3) unpack this wave's 16 rows in registers and score them
+        const int row = wave * 16 + n;
+        const uint8_t *rp = raw_lds + row * kRowBytes;
+        uint4 nib[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) nib[k] = *reinterpret_cast<const uint4 *>(rp + 64 * g + 16 * k);
+        const uint2 sc = *reinterpret_cast<const uint2 *>(rp + kScaleOff + 8 * g);
+        const uint4 rope = *reinterpret_cast<const uint4 *>(rp + kRopeOff + 16 * g);
+        half2_t s2[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t byte = ((k < 4 ? sc.x : sc.y) >> (8 * (k & 3))) & 0xFFu;
+            s2[k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(byte * 0x0101u, 1.0f, false);
+        }
+        float4_t acc[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+        _Float16 *vrow = v_lds + row * kVStride + 128 * g;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t d = (j & 3) == 0 ? nib[j >> 2].x : (j & 3) == 1 ? nib[j >> 2].y
+                             : (j & 3) == 2 ? nib[j >> 2].z : nib[j >> 2].w;
+            const half2_t sv = s2[j >> 1];
+            const half2_t e0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * sv;
+            const half2_t e1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * sv;
+            const half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * sv;
+            const half2_t e3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * sv;
+            const half8_t kb = join(e0, e1, e2, e3);
+            *reinterpret_cast<half8_t *>(vrow + 8 * j) = kb;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[mb][j], kb, acc[mb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 16; j < 18; ++j) {
+            const uint32_t d0 = (j == 16) ? rope.x : rope.z;
+            const uint32_t d1 = (j == 16) ? rope.y : rope.w;
+            const half8_t kb = join(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false),
+                                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true),
+                                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false),
+                                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[mb][j], kb, acc[mb], 0, 0, 0);
+        }
+
+        // (4) tile maxima per head (this wave's rows), exchanged through LDS
+        const bool valid = tile * kTile + row < n_valid;
+        float x[MB][4];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                x[mb][r] = valid ? acc[mb][r] * scale_log2 : -INFINITY;
+                float mx = x[mb][r];
+                mx = fmaxf(mx, __shfl_xor(mx, 1, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 2, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 4, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 8, 16));
+                if (n == 0) wmax_lds[wave][mb * 16 + 4 * g + r] = mx;
+            }
+        }
+        __syncthreads();
+
+        // (5) new running max, weights, rescale of the accumulators
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int h = mb * 16 + 4 * g + r;
+                const float mt = fmaxf(fmaxf(wmax_lds[0][h], wmax_lds[1][h]),
+                                       fmaxf(wmax_lds[2][h], wmax_lds[3][h]));
+                const float m_new = fmaxf(m_run[mb][r], mt);
+                float alpha, p;
+                if (m_new == -INFINITY) {
+                    alpha = 1.0f;
+                    p = 0.0f;
+                } else {
+                    alpha = exp2f(m_run[mb][r] - m_new);
+                    p = exp2f(x[mb][r] - m_new);
+                }
+                m_run[mb][r] = m_new;
+                const _Float16 ph = (_Float16)p;
+                p_lds[h * kPStride + row] = ph;
+                float ps = (float)ph;  // the normaliser sums the weights actually used
+                ps += __shfl_xor(ps, 1, 16);
+                ps += __shfl_xor(ps, 2, 16);
+                ps += __shfl_xor(ps, 4, 16);
+                ps += __shfl_xor(ps, 8, 16);
+                l_run[mb][r] = l_run[mb][r] * alpha + ps;
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) o[mb][nb][r] *= alpha;
+            }
+        }
+        __syncthreads();
+
+        // (6) value contraction: this wave's 128 output columns, all 64 rows
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            half8_t pa[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                pa[mb] = *reinterpret_cast<const half8_t *>(p_lds + (mb * 16 + n) * kPStride +
+                                                            32 * ks + 8 * g);
+            const int vr = 32 * ks + 8 * g + (n >> 2);
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const int col = 128 * wave + 16 * nb + 4 * (n & 3);
+                typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+                const lds_fp16x4 *p0 = (const lds_fp16x4 *)(
+                    (__attribute__((address_space(3))) _Float16 *)(v_lds + vr * kVStride + col));
+                const lds_fp16x4 *p1 = (const lds_fp16x4 *)(
+                    (__attribute__((address_space(3))) _Float16 *)(v_lds + (vr + 4) * kVStride + col));
+                const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)p0);
+                const fp16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)p1);
+                half8_t vb;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { vb[i] = (_Float16)lo[i]; vb[4 + i] = (_Float16)hi[i]; }
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[mb], vb, o[mb][nb], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- epilogue: combine the waves' row sums ----
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (n == 0) lsum_lds[wave][mb * 16 + 4 * g + r] = l_run[mb][r];
+    __syncthreads();
+    float l_tot[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int h = mb * 16 + 4 * g + r;
+            l_tot[mb][r] = lsum_lds[0][h] + lsum_lds[1][h] + lsum_lds[2][h] + lsum_lds[3][h];
+        }
+
+    const float ln2 = 0.69314718055994530942f;
+    if (splits == 1) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int head = hg * HG + mb * 16 + 4 * g + r;
+                const float inv = l_tot[mb][r] > 0.f ? 1.0f / l_tot[mb][r] : 0.f;
+                float *orow = out + ((int64_t)b * heads + head) * kLatent + 128 * wave + n;
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) orow[16 * nb] = o[mb][nb][r] * inv;
+                if (wave == 0 && n == 0)
+                    lse[(int64_t)b * heads + head] =
+                        l_tot[mb][r] > 0.f ? (m_run[mb][r] + log2f(l_tot[mb][r])) * ln2 : -INFINITY;
+            }
+        return;
+    }
+
+    // ---- split: publish the partial, last arrival merges ----
+    const size_t pfl = (size_t)HG * kLatent + 2 * HG;
+    float *part = ws_partials + ((size_t)unit * splits + split) * pfl;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int h = mb * 16 + 4 * g + r;
+            float *prow = part + (size_t)h * kLatent + 128 * wave + n;
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) prow[16 * nb] = o[mb][nb][r];
+            if (wave == 0 && n == 0) {
+                part[(size_t)HG * kLatent + h] = m_run[mb][r];
+                part[(size_t)HG * kLatent + HG + h] = l_tot[mb][r];
+            }
+        }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(ws_counters + unit, 1, __ATOMIC_ACQ_REL,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == splits - 1;
+        if (last)
+            __hip_atomic_store(ws_counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        flag_lds = last;
+    }
+    __syncthreads();
+    if (!flag_lds) return;
+    __threadfence();
+
+    const float *base = ws_partials + (size_t)unit * splits * pfl;
+    for (int e = tid; e < HG * kLatent; e += kThreads) {
+        const int h = e / kLatent;
+        const int d = e - h * kLatent;
+        float M = -INFINITY;
+        for (int s = 0; s < splits; ++s) M = fmaxf(M, base[s * pfl + (size_t)HG * kLatent + h]);
+        float Ls = 0.f, acc = 0.f;
+        if (M != -INFINITY) {
+            for (int s = 0; s < splits; ++s) {
+                const float *ps = base + s * pfl;
+                const float w = exp2f(ps[(size_t)HG * kLatent + h] - M);
+                Ls += w * ps[(size_t)HG * kLatent + HG + h];
+                acc += w * ps[(size_t)h * kLatent + d];
+            }
+        }
+        const int head = hg * HG + h;
+        out[((int64_t)b * heads + head) * kLatent + d] = Ls > 0.f ? acc / Ls : 0.f;
+        if (d == 0)
+            lse[(int64_t)b * heads + head] = Ls > 0.f ? (M + log2f(Ls)) * ln2 : -INFINITY;
+    }
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int batch, int heads, int topk) {
+    DecodePlan p;
+    p.heads_per_group = heads >= 32 ? 32 : 16;
+    p.groups = heads / p.heads_per_group;
+    const int units = batch * p.groups;
+    const int target = 256;  // one workgroup per CU
+    int s = (target + units - 1) / units;
+    const int max_s = (topk + kTile - 1) / kTile;
+    s = s < 1 ? 1 : s;
+    s = s > max_s ? max_s : s;
+    s = s > 16 ? 16 : s;
+    p.splits = s;
+    p.per_split = (topk + s - 1) / s;
+    p.partial_floats = (size_t)p.heads_per_group * kLatent + 2 * p.heads_per_group;
+    if (s == 1) {
+        p.workspace_bytes = 0;
+    } else {
+        // counters first, at a fixed place whatever the shape, so one zeroed
+        // buffer serves calls of any shape; partial results after them
+        const size_t part = (size_t)units * s * p.partial_floats * sizeof(float);
+        p.workspace_bytes = kCounterBytes + ((part + 255) & ~(size_t)255);
+    }
+    return p;
+}
+
+hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int64_t num_pages,
+                                    const int32_t *page_table, int32_t max_pages,
+                                    const int32_t *seq_lens, const int32_t *topk_idx,
+                                    int32_t batch, int32_t heads, int32_t topk, float scale,
+                                    float *out, float *lse, void *workspace,
+                                    const DecodePlan &plan, hipStream_t stream) {
+    const int units = batch * plan.groups;
+    const int blocks = ((units + 7) / 8) * 8 * plan.splits;
+    float *partials = nullptr;
+    int32_t *counters = nullptr;
+    if (plan.splits > 1) {
+        counters = static_cast<int32_t *>(workspace);
+        partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kCounterBytes);
+    }
+    const float scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    if (plan.heads_per_group == 32) {
+        hipLaunchKernelGGL(sparse_mla_decode_kernel<32>, dim3(blocks), dim3(kThreads), 0, stream,
+                           q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,
+                           topk, scale_log2, out, lse, partials, counters, units, plan.groups,
+                           plan.splits, plan.per_split);
+    } else {
+        hipLaunchKernelGGL(sparse_mla_decode_kernel<16>, dim3(blocks), dim3(kThreads), 0, stream,
+                           q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,
+                           topk, scale_log2, out, lse, partials, counters, units, plan.groups,
+                           plan.splits, plan.per_split);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace smla

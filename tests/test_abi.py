@@ -1,0 +1,115 @@
+"""CPU checks of the C ABI: the library loads, exports what include/smla.h
+declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    import sparse_mla_decode_amd as smla
+    names = declared_functions()
+    assert set(names) == set(smla.EXPORTS), names
+    raw = ctypes.CDLL(smla.LIB_PATH)
+    for name in names:
+        assert hasattr(raw, name), name
+
+
+def test_strerror_and_version():
+    import sparse_mla_decode_amd as smla
+    for code in list(smla.ERRORS) + [-99, 5]:
+        s = smla.lib.smla_strerror(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert smla.version() >= 100
+
+
+def test_workspace_sizes():
+    import sparse_mla_decode_amd as smla
+    assert smla.decode_workspace_bytes(0, 64, 2048) == 0
+    assert smla.decode_workspace_bytes(4, 32, 2048) == 0          # heads unsupported
+    assert smla.decode_workspace_bytes(4, 64, 4096) == 0          # topk too large
+    # batch 64 x 64 heads: 2 head groups x 2 splits of 32-head partials
+    ws = smla.decode_workspace_bytes(64, 64, 2048)
+    assert ws >= 64 * 2 * 2 * (32 * 512 + 64) * 4
+    assert ws % 256 == 0
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails host-side validation
+
+
+def _decode(**kw):
+    import sparse_mla_decode_amd as smla
+    a = dict(q=FAKE, cache=FAKE, num_pages=10, page_table=FAKE, max_pages=4, seq_lens=FAKE,
+             topk_indices=FAKE, batch=2, heads=16, topk=64, scale=0.04, out=FAKE, lse=FAKE,
+             ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return smla.lib.smla_sparse_mla_decode(a["q"], a["cache"], a["num_pages"], a["page_table"],
+                                           a["max_pages"], a["seq_lens"], a["topk_indices"],
+                                           a["batch"], a["heads"], a["topk"], a["scale"],
+                                           a["out"], a["lse"], a["ws"], a["ws_bytes"],
+                                           a["stream"])
+
+
+def test_decode_rejects_bad_arguments():
+    assert _decode(heads=32) == -3
+    assert _decode(heads=8) == -3
+    assert _decode(topk=0) == -2
+    assert _decode(topk=2049) == -2
+    assert _decode(batch=0) == -2
+    assert _decode(max_pages=0) == -2
+    assert _decode(num_pages=0) == -2
+    assert _decode(num_pages=(1 << 25) + 1) == -2
+    assert _decode(q=None) == -1
+    assert _decode(cache=None) == -1
+    assert _decode(lse=None) == -1
+    assert _decode(q=FAKE + 2) == -4
+    assert _decode(out=FAKE + 4) == -4
+    assert _decode(cache=FAKE + 16) == -4
+    assert _decode(topk_indices=FAKE + 1) == -4
+    # batch 1 x 64 heads needs split partials: missing or short workspace
+    assert _decode(batch=1, heads=64, topk=2048, ws=None, ws_bytes=0) == -5
+    assert _decode(batch=1, heads=64, topk=2048, ws_bytes=1024) == -5
+    assert _decode(batch=1, heads=64, topk=2048, ws=FAKE + 64) == -4
+    # valid arguments on a machine without a gfx950 device: refused, nothing launched
+    import torch
+    if not torch.cuda.is_available():
+        assert _decode() == -7
+
+
+def _append(**kw):
+    import sparse_mla_decode_amd as smla
+    a = dict(rows=FAKE, n=5, slots=FAKE, cache=FAKE, num_pages=3, stream=None)
+    a.update(kw)
+    return smla.lib.smla_kv_quant_append(a["rows"], a["n"], a["slots"], a["cache"],
+                                         a["num_pages"], a["stream"])
+
+
+def test_append_rejects_bad_arguments():
+    assert _append(n=-1) == -2
+    assert _append(num_pages=0) == -2
+    assert _append(rows=None) == -1
+    assert _append(slots=None) == -1
+    assert _append(rows=FAKE + 8) == -4
+    assert _append(cache=FAKE + 128) == -4
+    assert _append(slots=FAKE + 2) == -4
+    assert _append(n=0, rows=None) == 0          # nothing to do, nothing touched
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import sparse_mla_decode_amd as smla
+    rows = torch.zeros((2, 576), dtype=torch.bfloat16)
+    slots = torch.zeros(2, dtype=torch.int32)
+    cache = torch.zeros((1, 64, 352), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        smla.kv_quant_append(rows, slots, cache)

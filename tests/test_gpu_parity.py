@@ -1,0 +1,288 @@
+"""GPU parity of the HIP path against the CPU oracle (through the C ABI).
+
+Bars: cache bytes bit-exact; decode out within 2e-2 relative L2 over the
+whole [B,H,512] tensor and lse within 1e-3 absolute (max over (b,h)).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from cases import (gpu_cache, gpu_decode, lse_err, note, oracle_cache, oracle_decode, rel_l2,
+                   small_case, to_dev_bf16, worst_head_rel)
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 2e-2
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def smla():
+    import sparse_mla_decode_amd as m
+    return m
+
+
+def _append_and_read(smla, dev, bits: np.ndarray) -> np.ndarray:
+    n = bits.shape[0]
+    pages = (n + 63) // 64
+    cache = torch.zeros((pages, 64, 352), dtype=torch.uint8, device=dev)
+    slots = torch.arange(n, dtype=torch.int32, device=dev)
+    smla.kv_quant_append(to_dev_bf16(bits, dev), slots, cache)
+    torch.cuda.synchronize(dev)
+    return cache.view(-1, 352)[:n].cpu().numpy()
+
+
+# --------------------------------------------------------------------------
+# kv_quant_append: bit-exact
+# --------------------------------------------------------------------------
+
+def test_quant_random_rows_bit_exact(dev, smla):
+    note("quant random rows n=5000")
+    g = torch.Generator().manual_seed(1)
+    x = torch.randn((5000, 576), generator=g)
+    x[:1000] *= 8
+    x[1000:2000] *= 1e-3
+    x[2000:2500] *= 300.0
+    x[2500:2600, 100:300] = 0
+    bits = wl.bf16_bits(x.to(torch.bfloat16))
+    bits[2600:2610, :64] = 0x8000                       # -0 blocks
+    got = _append_and_read(smla, dev, bits)
+    want = oracle.quant_rows(bits)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:10]
+
+
+def test_quant_every_amax_bit_exact(dev, smla):
+    """Every positive finite BF16 value as a block maximum, the other 15 values
+    of the block drawn at or below it; covers every scale decision."""
+    note("quant every bf16 amax")
+    bits_all = np.arange(0x0001, 0x7F80, dtype=np.uint32).astype(np.uint16)   # positive finite
+    nblk = bits_all.size
+    rows = (nblk + 31) // 32
+    rng = np.random.default_rng(2)
+    x = np.zeros((rows * 32, 16), dtype=np.uint16)
+    amax = np.concatenate([bits_all, bits_all[:rows * 32 - nblk]])
+    # values <= amax in magnitude: random bit patterns below amax (monotone in bits)
+    lower = (rng.random((rows * 32, 15)) * amax[:, None].astype(np.float64)).astype(np.uint16)
+    x[:, 0] = amax
+    x[:, 1:] = lower
+    x[:, 1:] |= (rng.integers(0, 2, size=(rows * 32, 15)) << 15).astype(np.uint16)   # signs
+    for r in range(rows * 32):
+        x[r] = x[r, rng.permutation(16)] if r % 5 == 0 else x[r]
+    lat = x.reshape(rows, 512)
+    rope = rng.integers(0, 0x7F80, size=(rows, 64)).astype(np.uint16)
+    bits = np.concatenate([lat, rope], axis=1)
+    got = _append_and_read(smla, dev, bits)
+    want = oracle.quant_rows(bits)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:10]
+
+
+def test_quant_every_bf16_rope_and_e2m1_ties(dev, smla):
+    note("quant every bf16 rope value, e2m1 ties")
+    finite = np.array([b for b in range(65536) if ((b >> 7) & 0xFF) != 0xFF], dtype=np.uint16)
+    nrows = (finite.size + 63) // 64
+    rope = np.resize(finite, nrows * 64).reshape(nrows, 64)
+    # latent: blocks whose values sit exactly on e2m1 midpoints of their own scale
+    lat = np.zeros((nrows, 512), dtype=np.uint16)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.5, 3.0, 4.0, 2.0, 1.0,
+                     1.5, 0.0, 6.0])
+    scales = oracle.e4m3_value(np.arange(1, 0x7F, dtype=np.uint8))
+    for r in range(nrows):
+        S = scales[r % scales.size]
+        vals = (mids * S).astype(np.float32)            # exact: <= 7 significant bits
+        u = vals.view(np.uint32)
+        assert not (u & 0xFFFF).any()
+        blk = (u >> 16).astype(np.uint16)
+        blk[::3] |= 0x8000
+        lat[r] = np.tile(blk, 32)
+    bits = np.concatenate([lat, rope], axis=1)
+    got = _append_and_read(smla, dev, bits)
+    want = oracle.quant_rows(bits)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:10]
+
+
+def test_quant_slot_mapping_skips_and_leaves_others(dev, smla):
+    note("quant slot mapping")
+    n = 300
+    bits = wl.bf16_bits(torch.randn((n, 576), generator=torch.Generator().manual_seed(3))
+                        .to(torch.bfloat16))
+    pages = 6
+    slots = np.random.default_rng(4).permutation(pages * 64)[:n].astype(np.int32)
+    slots[::7] = -1
+    slots[5] = pages * 64            # one past the end
+    slots[6] = 2 ** 31 - 1
+    cache = torch.full((pages, 64, 352), 0xAB, dtype=torch.uint8, device=dev)
+    smla.kv_quant_append(to_dev_bf16(bits, dev), torch.as_tensor(slots, device=dev), cache)
+    torch.cuda.synchronize(dev)
+    want = np.full((pages, 64, 352), 0xAB, dtype=np.uint8)
+    oracle.kv_quant_append(bits, slots, want)
+    assert np.array_equal(cache.cpu().numpy(), want)
+
+
+# --------------------------------------------------------------------------
+# sparse_mla_decode: small problems, several tiles, ragged tails
+# --------------------------------------------------------------------------
+
+DECODE_CASES = [
+    # (batch, heads, lens, topk, extra kwargs)
+    (1, 16, [4096], 256, {}),
+    (3, 16, [3000, 777, 64], 512, {}),
+    (2, 64, [5000, 1500], 2048, {}),
+    (5, 64, [2100, 300, 64, 1, 4000], 2048, {}),
+    (4, 16, [2500, 2500, 90, 700], 2048, dict(pad=1500)),
+    (2, 16, [1000, 1000], 100, dict(dup=10, junk=5)),
+    (2, 64, [333, 129], 17, dict(junk=3)),
+    (1, 64, [70000], 2048, {}),
+    (6, 16, [64, 65, 127, 128, 129, 1], 64, {}),
+]
+
+
+@pytest.mark.parametrize("batch,heads,lens,topk,kw", DECODE_CASES,
+                         ids=["B%d_H%d_K%d_%d" % (c[0], c[1], c[3], i)
+                              for i, c in enumerate(DECODE_CASES)])
+def test_decode_matches_oracle(dev, smla, batch, heads, lens, topk, kw):
+    case = small_case(batch, heads, lens, topk, seed=batch * 100 + topk, **kw)
+    note("decode B=%d H=%d lens=%s K=%d %s" % (batch, heads, lens, topk, kw))
+    cache_d = gpu_cache(case, dev, smla)
+    cache_o = oracle_cache(case)
+    assert np.array_equal(cache_d.cpu().numpy(), cache_o)
+    out, lse = gpu_decode(case, cache_d, dev, smla)
+    ref_o, ref_l = oracle_decode(case, cache_o)
+    e_out, e_worst, e_lse = rel_l2(out, ref_o), worst_head_rel(out, ref_o), lse_err(lse, ref_l)
+    note("  rel_l2 %.3e worst-head %.3e lse %.3e" % (e_out, e_worst, e_lse))
+    assert np.isfinite(out).all()
+    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+
+
+def test_decode_empty_selections(dev, smla):
+    note("decode empty selections")
+    case = small_case(3, 64, [100, 50, 10], 64, seed=5)
+    case["topk"][:] = -1
+    case["topk"][1, :5] = [50, 51, 99, -3, 10 ** 6]     # all out of range for L=50
+    cache_d = gpu_cache(case, dev, smla)
+    out, lse = gpu_decode(case, cache_d, dev, smla)
+    assert not out.any()
+    assert np.isneginf(lse).all()
+    # a page id outside the cache is skipped too
+    case2 = small_case(1, 16, [128], 64, seed=6)
+    case2["pt"][0, 1] = case2["num_pages"] + 3          # tokens 64..127
+    case2["topk"][0] = np.arange(64, 128)
+    out2, lse2 = gpu_decode(case2, gpu_cache(small_case(1, 16, [128], 64, seed=6), dev, smla),
+                            dev, smla)
+    assert not out2.any() and np.isneginf(lse2).all()
+
+
+def test_decode_deterministic(dev, smla):
+    note("decode determinism")
+    case = small_case(2, 64, [3000, 2000], 2048, seed=7)
+    cache_d = gpu_cache(case, dev, smla)
+    a = gpu_decode(case, cache_d, dev, smla)
+    b = gpu_decode(case, cache_d, dev, smla)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_decode_invariances(dev, smla):
+    """Page relocation is bit-identical; list permutation and -1 padding only
+    move rounding."""
+    note("decode invariances")
+    case = small_case(2, 16, [2000, 900], 1024, seed=8, pad=200)
+    cache_d = gpu_cache(case, dev, smla)
+    base_o, base_l = gpu_decode(case, cache_d, dev, smla)
+    # relocate pages
+    P = case["num_pages"]
+    move = np.random.default_rng(9).permutation(P)
+    c2 = torch.zeros_like(cache_d)
+    c2[torch.as_tensor(move, device=dev)] = cache_d
+    case_m = dict(case)
+    case_m["pt"] = np.where(case["pt"] >= 0, move[np.maximum(case["pt"], 0)], -1).astype(np.int32)
+    o2, l2 = gpu_decode(case_m, c2, dev, smla)
+    assert np.array_equal(o2, base_o) and np.array_equal(l2, base_l)
+    # permute the lists
+    case_p = dict(case)
+    case_p["topk"] = case["topk"][:, np.random.default_rng(10).permutation(case["topk"].shape[1])]
+    o3, l3 = gpu_decode(case_p, cache_d, dev, smla)
+    # a different order regroups rows into tiles, which moves the running max
+    # each weight is rounded to f16 against: each weight moves by <= 2^-11
+    # relative, so out moves by <= ~2^-10 relative and lse by <= ~2^-11
+    assert rel_l2(o3, base_o.astype(np.float64)) < 1e-3
+    assert np.max(np.abs(l3 - base_l)) < 1e-3
+
+
+# --------------------------------------------------------------------------
+# full-size workloads: all queries on the GPU, sampled sequences on the oracle
+# --------------------------------------------------------------------------
+
+def _full_workload_check(dev, smla, name, sample, seed=0):
+    w = wl.WORKLOADS[name]
+    lens = wl.context_lengths(w, seed)
+    pt, num_pages = wl.build_page_table(w, lens, seed)
+    note("full %s: %d pages (%.2f GB)" % (name, num_pages, num_pages * 22528 / 1e9))
+    cache = torch.zeros((num_pages, 64, 352), dtype=torch.uint8, device=dev)
+    append = lambda rows, slots: smla.kv_quant_append(rows, slots, cache)
+    wl.fill_cache(w, seed, lens, pt, append, dev, tail=w.append_tail)
+    if w.append_tail:
+        rows, slots = wl.tail_rows(w, seed, lens, pt, dev, w.append_tail)
+        note("  append %d tail rows" % rows.shape[0])
+        append(rows, slots)
+    tk = wl.topk_indices(w, lens, seed)
+    q = wl.queries(w, seed, device=dev)
+    note("  decode")
+    out, lse = smla.sparse_mla_decode(q, cache, torch.as_tensor(pt, device=dev),
+                                      torch.as_tensor(lens.astype(np.int32), device=dev),
+                                      torch.as_tensor(tk, device=dev), w.softmax_scale)
+    torch.cuda.synchronize(dev)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    qbits = wl.bf16_bits(q)
+    flat = cache.view(-1, 352)
+    worst = 0.0
+    for b in sample:
+        sel = tk[b][tk[b] >= 0].astype(np.int64)
+        rows = wl.rows_at(w, seed, b, sel, device=dev)
+        rbits = wl.bf16_bits(rows)
+        mine = oracle.quant_rows(rbits)
+        slots = wl.slots_for(pt, b, 0, int(lens[b]))[sel].astype(np.int64)
+        got_bytes = flat[torch.as_tensor(slots, device=dev)].cpu().numpy()
+        assert np.array_equal(got_bytes, mine), "cache bytes differ for sequence %d" % b
+        # the oracle on the selected rows alone, in list order
+        n = sel.size
+        mini = np.zeros(((n + 63) // 64, 64, 352), dtype=np.uint8)
+        mini.reshape(-1, 352)[:n] = mine
+        ro, rl = oracle.sparse_mla_decode(qbits[b:b + 1], mini,
+                                          np.arange((n + 63) // 64, dtype=np.int32)[None],
+                                          np.array([n]), np.arange(n, dtype=np.int32)[None],
+                                          w.softmax_scale)
+        e_out, e_lse = rel_l2(out[b:b + 1], ro), lse_err(lse[b:b + 1], rl)
+        note("  seq %d: rel_l2 %.3e lse %.3e" % (b, e_out, e_lse))
+        assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+        worst = max(worst, e_out)
+    del cache
+    torch.cuda.empty_cache()
+    return worst
+
+
+def test_full_tp4(dev, smla):
+    _full_workload_check(dev, smla, "tp4", sample=[0, 17, 31])
+
+
+def test_full_allheads(dev, smla):
+    _full_workload_check(dev, smla, "allheads", sample=[0, 40, 63])
+
+
+def test_full_ragged(dev, smla):
+    w = wl.WORKLOADS["ragged"]
+    lens = wl.context_lengths(w, 0)
+    short = [int(np.argmin(lens))]
+    _full_workload_check(dev, smla, "ragged", sample=short + [0, 127])
+
+
+def test_full_million(dev, smla):
+    _full_workload_check(dev, smla, "million", sample=[0, 7])

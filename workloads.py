@@ -240,6 +240,31 @@ def iter_fill(w: Workload, seed: int, lens: np.ndarray, page_table: np.ndarray,
             t += n
 
 
+def fill_cache(w: Workload, seed: int, lens: np.ndarray, page_table: np.ndarray,
+               append, device, tail: int = 0) -> int:
+    """Fill tokens [0, L_b - tail) of every sequence through ``append(rows,
+    slots)`` (the caller's quantise-append).  Returns the number of rows."""
+    total = 0
+    for b, t0, rows, slots in iter_fill(w, seed, lens, page_table, device, tail):
+        append(rows, torch.as_tensor(slots, device=device))
+        total += rows.shape[0]
+    return total
+
+
+def tail_rows(w: Workload, seed: int, lens: np.ndarray, page_table: np.ndarray, device,
+              tail: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Rows and slots of the last min(tail, L_b) tokens of every sequence,
+    concatenated: the new tokens one append step writes."""
+    rows, slots = [], []
+    for b, L in enumerate(lens):
+        L = int(L)
+        t0 = max(L - tail, 0)
+        rows.append(kv_rows(w, seed, b, t0, L - t0, device))
+        slots.append(slots_for(page_table, b, t0, L - t0))
+    return (torch.cat(rows, 0),
+            torch.as_tensor(np.concatenate(slots), device=device))
+
+
 def bf16_bits(x: torch.Tensor) -> np.ndarray:
     """BF16 tensor -> numpy uint16 bit patterns (host copy)."""
     return x.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
