@@ -1,0 +1,249 @@
+"""Benchmark of the sparse NVFP4-MLA decode hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: quantise-append of the
+newest token's row of every sequence, then sparse MLA decode of one query per
+sequence over its top-k rows.  Inputs are resident in HBM before timing
+starts.  The timed loop rotates through independent (q, top-k) sets so that
+the rows a step reads are not the rows the previous steps left in the 256 MB
+Infinity Cache.
+
+Prints ONE JSON line (metric, value = effective KV GB/s over the step, ...,
+roofline of the decode kernel, cpu_baseline of the oracle on host cores).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense FP16/BF16 matrix, published
+ROW_BYTES = 352
+APPEND_BYTES_PER_ROW = 576 * 2 + ROW_BYTES     # BF16 row read + NVFP4 row written
+FLOPS_PER_HEAD_ROW = 2 * 576 + 2 * 512         # score + value contraction
+CACHE_BYTES_MALL = 256 << 20
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "sparse_mla_decode_amd", "csrc", "sparse_mla_decode.hip")
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("sparse_mla_decode.hip", "smla_internal.h"):
+        with open(os.path.join(ROOT, "sparse_mla_decode_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, or None
+    when the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = d.get(workload)
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seed, lens, tk_np, qbits, budget_s, dev):
+    """Time the oracle's decode on host cores over as many sequences as fit in
+    roughly budget_s seconds (at least one)."""
+    import torch
+    import oracle
+    import workloads as wl
+    cores = len(os.sched_getaffinity(0))
+    cores = min(cores, 16)
+    done, t_used, kv_bytes = 0, 0.0, 0
+    order = list(range(w.batch))
+    for b in order:
+        sel = tk_np[b][tk_np[b] >= 0].astype(np.int64)
+        sel = sel[sel < lens[b]]
+        n = sel.size
+        rows = oracle.quant_rows(wl.bf16_bits(wl.rows_at(w, seed, b, sel, device=dev)))
+        mini = np.zeros(((max(n, 1) + 63) // 64, 64, 352), dtype=np.uint8)
+        mini.reshape(-1, 352)[:n] = rows
+        pt = np.arange(mini.shape[0], dtype=np.int32)[None]
+        t0 = time.perf_counter()
+        oracle.sparse_mla_decode(qbits[b:b + 1], mini, pt, np.array([n]),
+                                 np.arange(n, dtype=np.int32)[None], w.softmax_scale,
+                                 nthreads=cores)
+        t_used += time.perf_counter() - t0
+        done += 1
+        kv_bytes += n * ROW_BYTES
+        if t_used >= budget_s:
+            break
+    gbps = kv_bytes / t_used / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "oracle decode (fp64 C, OpenMP over heads) of %d of %d sequences "
+                      "(%d heads, %d selected rows each), %.1f s; %.2f queries/s"
+                      % (done, w.batch, w.heads, int(np.mean([min(w.topk, L) for L in lens])),
+                         t_used, done / t_used)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="allheads")
+    ap.add_argument("--sets", type=int, default=0, help="rotating (q, top-k) sets (0 = auto)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 256 MiB device copy first (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_mla_decode_amd as smla
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.WORKLOADS[args.workload]
+    seed = args.seed
+    lens = wl.context_lengths(w, seed)
+    pt_np, num_pages = wl.build_page_table(w, lens, seed)
+    log("workload %s: %s; cache %d pages (%.2f GB)" % (w.name, w.desc, num_pages,
+                                                       num_pages * 22528 / 1e9))
+    if args.calibrate_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b_ = torch.empty_like(a)
+        b_.copy_(a)
+        torch.cuda.synchronize()
+        del a, b_
+
+    cache = torch.zeros((num_pages, 64, 352), dtype=torch.uint8, device=dev)
+    append = lambda rows, slots: smla.kv_quant_append(rows, slots, cache)
+    t0 = time.time()
+    wl.fill_cache(w, seed, lens, pt_np, append, dev, tail=w.append_tail)
+    # the step's append: the newest min(tail, L) tokens (ragged, million) or
+    # the newest token of every sequence (decode steps of the other workloads)
+    step_tail = w.append_tail if w.append_tail else 1
+    step_rows, step_slots = wl.tail_rows(w, seed, lens, pt_np, dev, step_tail)
+    append(step_rows, step_slots)
+    torch.cuda.synchronize()
+    log("cache filled in %.1f s; step appends %d rows" % (time.time() - t0, step_rows.shape[0]))
+
+    pt = torch.as_tensor(pt_np, device=dev)
+    sl = torch.as_tensor(lens.astype(np.int32), device=dev)
+    per_call_bytes = int(sum(min(w.topk, int(L)) for L in lens)) * ROW_BYTES
+    sets = args.sets or max(4, math.ceil(2 * CACHE_BYTES_MALL / max(per_call_bytes, 1)) + 1)
+    qs, tks, nvalid = [], [], []
+    for s in range(sets):
+        tk_np = wl.topk_indices(w, lens, seed, set_id=s)
+        nvalid.append(int((tk_np >= 0).sum()))
+        tks.append(torch.as_tensor(tk_np, device=dev))
+        qs.append(wl.queries(w, seed, set_id=s, device=dev))
+    out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device=dev)
+    ws_bytes = smla.decode_workspace_bytes(w.batch, w.heads, w.topk)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    log("%d rotating sets, %.1f MB of selected rows each" % (sets, per_call_bytes / 1e6))
+
+    def step(i, ev=None):
+        s = i % sets
+        if ev is not None:
+            ev[0].record()
+        smla.kv_quant_append(step_rows, step_slots, cache)
+        if ev is not None:
+            ev[1].record()
+        smla.sparse_mla_decode(qs[s], cache, pt, sl, tks[s], w.softmax_scale, out=out,
+                               lse=lse, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    app_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    ms_per_step = t_total * 1e3 / args.steps
+
+    # algorithmic work per step (mean over the sets the timed steps used)
+    used = [(args.warmup + i) % sets for i in range(args.steps)]
+    dec_bytes = float(np.mean([nvalid[s] for s in used])) * ROW_BYTES
+    app_bytes = step_rows.shape[0] * APPEND_BYTES_PER_ROW
+    dec_flops = float(np.mean([nvalid[s] for s in used])) * w.heads * FLOPS_PER_HEAD_ROW
+    value = (dec_bytes + app_bytes) / (ms_per_step * 1e-3) / 1e9
+    dec_s = float(dec_ms.mean()) * 1e-3
+    dec_gbps = dec_bytes / dec_s / 1e9
+    dec_tflops = dec_flops / dec_s / 1e12
+    ai = w.heads * FLOPS_PER_HEAD_ROW / ROW_BYTES
+    ridge = MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    traffic = measured_traffic(w.name)
+    if ai >= ridge:
+        roof = {"bound": "mfma", "achieved": round(dec_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(dec_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                "traffic": traffic}
+    else:
+        roof = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
+
+    result = {
+        "metric": "sparse NVFP4-MLA decode: effective KV GB/s (% HBM peak) and queries/sec",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "topk": w.topk,
+                   "context": int(lens.max()) if w.ctx == 0 else w.ctx,
+                   "append_rows_per_step": int(step_rows.shape[0]),
+                   "rotating_sets": sets, "desc": w.desc},
+        "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "queries_per_s": round(w.batch / (ms_per_step * 1e-3), 1),
+        "decode_us": round(dec_s * 1e6, 2),
+        "decode_kv_GBps": round(dec_gbps, 1),
+        "decode_tflops": round(dec_tflops, 2),
+        "append_us": round(float(app_ms.mean()) * 1e3, 2),
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        tk0 = wl.topk_indices(w, lens, seed, set_id=0)
+        qbits = wl.bf16_bits(qs[0])
+        log("timing the oracle on host cores (budget %.0f s)" % args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, seed, lens, tk0, qbits, args.cpu_budget, dev)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -103,11 +103,8 @@ int smla_kv_quant_append(const void *rows_bf16, int64_t n, const int32_t *slot_m
 
 /*
  * Bytes of device workspace smla_sparse_mla_decode needs for this shape
- * (0 means none).  The first 512 KiB of a workspace hold ticket counters
- * (one per sequence and head group) at fixed offsets; the rest holds
- * per-split partial results.  The workspace must be zero-filled before its
- * first use; every call leaves the counters at zero again, so one zeroed
- * buffer can be reused by any number of calls of any shape on one stream.
+ * (0 means none).  The workspace holds per-split partial results between
+ * the two kernels a call may enqueue; its contents on entry do not matter.
  * Calls that overlap in time must not share a workspace.
  */
 size_t smla_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t topk);
@@ -138,8 +135,8 @@ size_t smla_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t topk);
  *   out           [batch][heads][512] fp32, 16-byte aligned (written)
  *   lse           [batch][heads] fp32 (written)
  *   workspace     >= smla_decode_workspace_bytes(batch, heads, topk) bytes,
- *                 256-byte aligned, zero-filled before first use (may be NULL
- *                 when that size is 0)
+ *                 256-byte aligned, any contents (may be NULL when that size
+ *                 is 0)
  *
  * Scores use FP16 operands (q and the decoded values; the decoded values are
  * exact in FP16) with FP32 accumulation; softmax weights are rounded to FP16

@@ -109,15 +109,12 @@ def decode_workspace_bytes(batch: int, heads: int, topk: int) -> int:
 
 
 def workspace_for(device: torch.device, nbytes: int, stream=None) -> torch.Tensor:
-    """A zero-initialised workspace of at least nbytes, cached per (device, stream).
-
-    The decode kernels leave the workspace's counters at zero after every call,
-    so the buffer is zeroed only when it is first allocated."""
+    """A workspace of at least nbytes, cached per (device, stream)."""
     key = (device.index, _stream_ptr(device, stream))
     with _ws_lock:
         ws = _workspaces.get(key)
         if ws is None or ws.numel() < nbytes:
-            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
             _workspaces[key] = ws
         return ws
 

@@ -21,10 +21,6 @@ constexpr int kRowBytes = kRopeOff + kRope;  // 352
 constexpr int kPageRows = 64;
 constexpr int kMaxTopk = 2048;
 constexpr int kMaxBatch = 65535;
-// Decode workspace: one int32 ticket counter per (sequence, head group) at a
-// fixed offset (sized for the largest batch and two head groups), then the
-// per-split partial results.
-constexpr size_t kCounterBytes = (size_t)131072 * sizeof(int32_t);
 
 // Decode launch plan shared by the host entry points and the kernel.
 struct DecodePlan {

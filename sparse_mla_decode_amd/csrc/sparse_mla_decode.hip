@@ -26,9 +26,13 @@
 //     into f16 weights; each wave then accumulates the value contraction for
 //     its 128 of the 512 output columns, reading weights and values from LDS
 //     (values through the transposing ds_read_b64_tr_b16);
-//   * splits of one (sequence, head group) are dispatched to the same XCD;
-//     each writes its partial (m, l, O) and the last to arrive (an atomic
-//     ticket) merges them in the same launch.
+//   * all workgroups of one sequence are dispatched to the same XCD so the
+//     head groups re-read each selected row from that XCD's L2;
+//   * when a sequence's top-k list is split over several workgroups, each
+//     writes its partial (m, l, O) to the workspace and a second, small
+//     kernel merges them (a merge inside the first launch would need an
+//     agent-scope release per workgroup, i.e. an L2 writeback, which costs
+//     more than the launch).
 #include "smla_internal.h"
 
 namespace smla {
@@ -46,6 +50,7 @@ constexpr int kPiecesPerThread = (kPieces + kThreads - 1) / kThreads;  // 6
 constexpr int kVStride = kLatent + 16;        // f16 elements per LDS value row (1056 B)
 constexpr int kPStride = kTile + 8;           // f16 elements per LDS weight row (144 B)
 constexpr int kKSteps = kDim / 32;            // 18 contraction steps of 32 for the scores
+constexpr float kSlack = 8.0f;                // log2 headroom before the running max moves
 
 __device__ __forceinline__ half8_t join(half2_t a, half2_t b, half2_t c, half2_t d) {
     half8_t r;
@@ -53,6 +58,32 @@ __device__ __forceinline__ half8_t join(half2_t a, half2_t b, half2_t c, half2_t
     r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
     return r;
 }
+
+// Reductions over the 16 lanes of a row with DPP lane moves (quad swaps,
+// half-row mirror, row mirror); every lane ends with the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
+                                                              0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+    x = fmaxf(x, dpp<0x140>(x));  // row_mirror
+    return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    return x;
+}
+
+// Partial results are streamed out with non-temporal stores so they do not
+// sit dirty in the L2 that the release fence has to write back.
+__device__ __forceinline__ void store_partial(float *p, float v) { __builtin_nontemporal_store(v, p); }
 
 __device__ __forceinline__ _Float16 bf16_to_f16(uint32_t h) {
     return (_Float16)__uint_as_float(h << 16);
@@ -65,8 +96,8 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                               int32_t max_pages, const int32_t *__restrict__ seq_lens,
                               const int32_t *__restrict__ topk_idx, int32_t heads, int32_t topk,
                               float scale_log2, float *__restrict__ out, float *__restrict__ lse,
-                              float *__restrict__ ws_partials, int32_t *__restrict__ ws_counters,
-                              int32_t units, int32_t groups, int32_t splits, int32_t per_split) {
+                              float *__restrict__ ws_partials, int32_t batch, int32_t groups,
+                              int32_t splits, int32_t per_split) {
     constexpr int MB = HG / 16;  // 16-head MFMA row blocks
     __shared__ __attribute__((aligned(16))) uint8_t raw_lds[kTile * kRowBytes];
     __shared__ __attribute__((aligned(16))) _Float16 v_lds[kTile * kVStride];
@@ -75,7 +106,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     __shared__ float wmax_lds[4][HG];
     __shared__ float lsum_lds[4][HG];
     __shared__ int32_t scan_lds[4];
-    __shared__ int32_t flag_lds;
+    __shared__ uint32_t flag_lds[4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -83,15 +114,16 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     const int n = lane & 15;   // row (scores) / column (values) within a 16-block
     const int g = lane >> 4;   // 8-element k group
 
-    // ---- which (sequence, head group, split) ----
+    // ---- which (sequence, head group, split): consecutive workgroups go to
+    // consecutive XCDs, so all workgroups of sequence b share XCD b % 8 ----
     const int id = blockIdx.x;
     const int xcd = id & 7;
     const int rest = id >> 3;
     const int split = rest % splits;
-    const int unit = (rest / splits) * 8 + xcd;
-    if (unit >= units) return;
-    const int b = unit / groups;
-    const int hg = unit % groups;
+    const int hg = (rest / splits) % groups;
+    const int b = (rest / splits / groups) * 8 + xcd;
+    if (b >= batch) return;
+    const int unit = b * groups + hg;
     const int e_begin = split * per_split;
     const int e_end = min(topk, e_begin + per_split);
 
@@ -249,57 +281,71 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                 acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[mb][j], kb, acc[mb], 0, 0, 0);
         }
 
-        // (4) tile maxima per head (this wave's rows), exchanged through LDS
+        // (4) scores in log2 units; decide whether any head's running max
+        // must move.  The running max only moves when a score exceeds it by
+        // more than kSlack (weights then stay <= 2^kSlack, fine in f16), so
+        // after the first tiles the max, the rescale and their cross-lane
+        // reductions are skipped.  The decision is shared by all waves.
         const bool valid = tile * kTile + row < n_valid;
         float x[MB][4];
+        bool over = false;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 x[mb][r] = valid ? acc[mb][r] * scale_log2 : -INFINITY;
-                float mx = x[mb][r];
-                mx = fmaxf(mx, __shfl_xor(mx, 1, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 2, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 4, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 8, 16));
-                if (n == 0) wmax_lds[wave][mb * 16 + 4 * g + r] = mx;
+                over |= x[mb][r] > m_run[mb][r] + kSlack;
             }
-        }
+        const uint64_t ballot = __ballot(over);
+        if (lane == 0) flag_lds[wave] = ballot != 0;
         __syncthreads();
-
-        // (5) new running max, weights, rescale of the accumulators
+        const bool move = (flag_lds[0] | flag_lds[1] | flag_lds[2] | flag_lds[3]) != 0;
+        if (move) {
+            // exact tile maxima per head, exchanged through LDS
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float mx = row16_max(x[mb][r]);
+                    if (n == 0) wmax_lds[wave][mb * 16 + 4 * g + r] = mx;
+                }
+            __syncthreads();
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int h = mb * 16 + 4 * g + r;
+                    const float mt = fmaxf(fmaxf(wmax_lds[0][h], wmax_lds[1][h]),
+                                           fmaxf(wmax_lds[2][h], wmax_lds[3][h]));
+                    const float m_new = fmaxf(m_run[mb][r], mt);
+                    // m_new = -inf only while nothing valid was seen: keep zeros
+                    const float alpha = (m_new == -INFINITY)
+                                            ? 1.0f
+                                            : __builtin_amdgcn_exp2f(m_run[mb][r] - m_new);
+                    m_run[mb][r] = m_new;
+                    l_run[mb][r] *= alpha;
+#pragma unroll
+                    for (int nb = 0; nb < 8; ++nb) o[mb][nb][r] *= alpha;
+                }
+        }
+
+        // (5) f16 weights to LDS; each lane keeps its own share of the sum
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int h = mb * 16 + 4 * g + r;
-                const float mt = fmaxf(fmaxf(wmax_lds[0][h], wmax_lds[1][h]),
-                                       fmaxf(wmax_lds[2][h], wmax_lds[3][h]));
-                const float m_new = fmaxf(m_run[mb][r], mt);
-                float alpha, p;
-                if (m_new == -INFINITY) {
-                    alpha = 1.0f;
-                    p = 0.0f;
-                } else {
-                    alpha = exp2f(m_run[mb][r] - m_new);
-                    p = exp2f(x[mb][r] - m_new);
-                }
-                m_run[mb][r] = m_new;
+                const float p = (m_run[mb][r] == -INFINITY)
+                                    ? 0.0f
+                                    : __builtin_amdgcn_exp2f(x[mb][r] - m_run[mb][r]);
                 const _Float16 ph = (_Float16)p;
                 p_lds[h * kPStride + row] = ph;
-                float ps = (float)ph;  // the normaliser sums the weights actually used
-                ps += __shfl_xor(ps, 1, 16);
-                ps += __shfl_xor(ps, 2, 16);
-                ps += __shfl_xor(ps, 4, 16);
-                ps += __shfl_xor(ps, 8, 16);
-                l_run[mb][r] = l_run[mb][r] * alpha + ps;
-#pragma unroll
-                for (int nb = 0; nb < 8; ++nb) o[mb][nb][r] *= alpha;
+                l_run[mb][r] += (float)ph;  // the normaliser sums the weights actually used
             }
-        }
         __syncthreads();
 
         // (6) value contraction: this wave's 128 output columns, all 64 rows
+        typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             half8_t pa[MB];
@@ -308,19 +354,20 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                 pa[mb] = *reinterpret_cast<const half8_t *>(p_lds + (mb * 16 + n) * kPStride +
                                                             32 * ks + 8 * g);
             const int vr = 32 * ks + 8 * g + (n >> 2);
+            fp16x4_t vlo[8], vhi[8];
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
                 const int col = 128 * wave + 16 * nb + 4 * (n & 3);
-                typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
-                const lds_fp16x4 *p0 = (const lds_fp16x4 *)(
-                    (__attribute__((address_space(3))) _Float16 *)(v_lds + vr * kVStride + col));
-                const lds_fp16x4 *p1 = (const lds_fp16x4 *)(
-                    (__attribute__((address_space(3))) _Float16 *)(v_lds + (vr + 4) * kVStride + col));
-                const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)p0);
-                const fp16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)p1);
+                vlo[nb] = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)(
+                    (__attribute__((address_space(3))) _Float16 *)(v_lds + vr * kVStride + col)));
+                vhi[nb] = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)(
+                    (__attribute__((address_space(3))) _Float16 *)(v_lds + (vr + 4) * kVStride + col)));
+            }
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
                 half8_t vb;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) { vb[i] = (_Float16)lo[i]; vb[4 + i] = (_Float16)hi[i]; }
+                for (int i = 0; i < 4; ++i) { vb[i] = (_Float16)vlo[nb][i]; vb[4 + i] = (_Float16)vhi[nb][i]; }
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
                     o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[mb], vb, o[mb][nb], 0, 0, 0);
@@ -328,12 +375,14 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         }
     }
 
-    // ---- epilogue: combine the waves' row sums ----
+    // ---- epilogue: combine the lanes' and the waves' shares of the sums ----
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (n == 0) lsum_lds[wave][mb * 16 + 4 * g + r] = l_run[mb][r];
+        for (int r = 0; r < 4; ++r) {
+            const float ls = row16_sum(l_run[mb][r]);
+            if (n == 0) lsum_lds[wave][mb * 16 + 4 * g + r] = ls;
+        }
     __syncthreads();
     float l_tot[MB][4];
 #pragma unroll
@@ -362,7 +411,9 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         return;
     }
 
-    // ---- split: publish the partial, last arrival merges ----
+    // ---- split: publish the partial; the merge kernel combines them ----
+    // Partial layout per (unit, split): O[HG][512] unnormalised, then m[HG]
+    // (running max, log2 units) and l[HG] (sum of weights).
     const size_t pfl = (size_t)HG * kLatent + 2 * HG;
     float *part = ws_partials + ((size_t)unit * splits + split) * pfl;
 #pragma unroll
@@ -378,47 +429,52 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                 part[(size_t)HG * kLatent + HG + h] = l_tot[mb][r];
             }
         }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(ws_counters + unit, 1, __ATOMIC_ACQ_REL,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        const int last = old == splits - 1;
-        if (last)
-            __hip_atomic_store(ws_counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        flag_lds = last;
-    }
-    __syncthreads();
-    if (!flag_lds) return;
-    __threadfence();
+}
 
+// Merge of the splits' partials: one thread per (unit, head, 4 columns), the
+// splits combined in split order (fixed, hence deterministic):
+//   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,  O = sum_s 2^(m_s - M) O_s / L.
+__global__ __launch_bounds__(256) void merge_splits_kernel(
+    const float *__restrict__ ws_partials, float *__restrict__ out, float *__restrict__ lse,
+    int32_t heads, int32_t hg_size, int32_t groups, int32_t splits, int32_t units) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)units * hg_size * (kLatent / 4);
+    if (idx >= total) return;
+    const int c4 = (int)(idx % (kLatent / 4));
+    const int h = (int)((idx / (kLatent / 4)) % hg_size);
+    const int unit = (int)(idx / ((int64_t)(kLatent / 4) * hg_size));
+    const size_t pfl = (size_t)hg_size * kLatent + 2 * hg_size;
     const float *base = ws_partials + (size_t)unit * splits * pfl;
-    for (int e = tid; e < HG * kLatent; e += kThreads) {
-        const int h = e / kLatent;
-        const int d = e - h * kLatent;
-        float M = -INFINITY;
-        for (int s = 0; s < splits; ++s) M = fmaxf(M, base[s * pfl + (size_t)HG * kLatent + h]);
-        float Ls = 0.f, acc = 0.f;
-        if (M != -INFINITY) {
-            for (int s = 0; s < splits; ++s) {
-                const float *ps = base + s * pfl;
-                const float w = exp2f(ps[(size_t)HG * kLatent + h] - M);
-                Ls += w * ps[(size_t)HG * kLatent + HG + h];
-                acc += w * ps[(size_t)h * kLatent + d];
-            }
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, base[s * pfl + (size_t)hg_size * kLatent + h]);
+    float L = 0.f;
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+        for (int s = 0; s < splits; ++s) {
+            const float *ps = base + s * pfl;
+            const float w = __builtin_amdgcn_exp2f(ps[(size_t)hg_size * kLatent + h] - M);
+            L += w * ps[(size_t)hg_size * kLatent + hg_size + h];
+            const float4_t v = *reinterpret_cast<const float4_t *>(ps + (size_t)h * kLatent + 4 * c4);
+            acc += w * v;
         }
-        const int head = hg * HG + h;
-        out[((int64_t)b * heads + head) * kLatent + d] = Ls > 0.f ? acc / Ls : 0.f;
-        if (d == 0)
-            lse[(int64_t)b * heads + head] = Ls > 0.f ? (M + log2f(Ls)) * ln2 : -INFINITY;
     }
+    const int b = unit / groups;
+    const int head = (unit % groups) * hg_size + h;
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    *reinterpret_cast<float4_t *>(out + ((int64_t)b * heads + head) * kLatent + 4 * c4) = acc * inv;
+    if (c4 == 0)
+        lse[(int64_t)b * heads + head] =
+            L > 0.f ? (M + log2f(L)) * 0.69314718055994530942f : -INFINITY;
 }
 
 }  // namespace
 
 DecodePlan plan_decode(int batch, int heads, int topk) {
     DecodePlan p;
-    p.heads_per_group = heads >= 32 ? 32 : 16;
+    // 16 heads per workgroup: one MFMA row block, the query and the
+    // accumulators fit in registers with room for the pipeline, and more
+    // workgroups per sequence share each selected row through the XCD's L2.
+    p.heads_per_group = 16;
     p.groups = heads / p.heads_per_group;
     const int units = batch * p.groups;
     const int target = 256;  // one workgroup per CU
@@ -433,10 +489,8 @@ DecodePlan plan_decode(int batch, int heads, int topk) {
     if (s == 1) {
         p.workspace_bytes = 0;
     } else {
-        // counters first, at a fixed place whatever the shape, so one zeroed
-        // buffer serves calls of any shape; partial results after them
         const size_t part = (size_t)units * s * p.partial_floats * sizeof(float);
-        p.workspace_bytes = kCounterBytes + ((part + 255) & ~(size_t)255);
+        p.workspace_bytes = (part + 255) & ~(size_t)255;
     }
     return p;
 }
@@ -447,26 +501,27 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
                                     int32_t batch, int32_t heads, int32_t topk, float scale,
                                     float *out, float *lse, void *workspace,
                                     const DecodePlan &plan, hipStream_t stream) {
-    const int units = batch * plan.groups;
-    const int blocks = ((units + 7) / 8) * 8 * plan.splits;
-    float *partials = nullptr;
-    int32_t *counters = nullptr;
-    if (plan.splits > 1) {
-        counters = static_cast<int32_t *>(workspace);
-        partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kCounterBytes);
-    }
+    const int blocks = ((batch + 7) / 8) * 8 * plan.groups * plan.splits;
+    float *partials = plan.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     const float scale_log2 = (float)((double)scale * 1.4426950408889634074);
     if (plan.heads_per_group == 32) {
         hipLaunchKernelGGL(sparse_mla_decode_kernel<32>, dim3(blocks), dim3(kThreads), 0, stream,
                            q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,
-                           topk, scale_log2, out, lse, partials, counters, units, plan.groups,
-                           plan.splits, plan.per_split);
+                           topk, scale_log2, out, lse, partials, batch, plan.groups, plan.splits,
+                           plan.per_split);
     } else {
         hipLaunchKernelGGL(sparse_mla_decode_kernel<16>, dim3(blocks), dim3(kThreads), 0, stream,
                            q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,
-                           topk, scale_log2, out, lse, partials, counters, units, plan.groups,
-                           plan.splits, plan.per_split);
+                           topk, scale_log2, out, lse, partials, batch, plan.groups, plan.splits,
+                           plan.per_split);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || plan.splits == 1) return e;
+    const int units = batch * plan.groups;
+    const int64_t threads = (int64_t)units * plan.heads_per_group * (kLatent / 4);
+    hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, partials, out, lse, heads, plan.heads_per_group, plan.groups,
+                       plan.splits, units);
     return hipGetLastError();
 }
 

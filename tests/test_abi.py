@@ -38,9 +38,11 @@ def test_workspace_sizes():
     assert smla.decode_workspace_bytes(0, 64, 2048) == 0
     assert smla.decode_workspace_bytes(4, 32, 2048) == 0          # heads unsupported
     assert smla.decode_workspace_bytes(4, 64, 4096) == 0          # topk too large
-    # batch 64 x 64 heads: 2 head groups x 2 splits of 32-head partials
-    ws = smla.decode_workspace_bytes(64, 64, 2048)
-    assert ws >= 64 * 2 * 2 * (32 * 512 + 64) * 4
+    # batch 64 x 64 heads: 256 workgroups of 16 heads, no split, no workspace
+    assert smla.decode_workspace_bytes(64, 64, 2048) == 0
+    # batch 1 x 64 heads: 4 head groups x 16 splits of 16-head partials
+    ws = smla.decode_workspace_bytes(1, 64, 2048)
+    assert ws >= 4 * 16 * (16 * 512 + 32) * 4
     assert ws % 256 == 0
 
 
