@@ -6,32 +6,37 @@
 // the selected 352-byte rows, unpack on chip, score, softmax and blend; -1
 // entries carry no data) and Prime Intellect's launch post, native-kernel
 // paragraph (FP16 operands, FP32 accumulation, partial results of the blocks
-// sharing a query merged in the same launch).  Every selected row serves all
+// sharing a query merged after the split).  Every selected row serves all
 // heads of the query: "GLM-5.3 PCP/DCP long-context on H200", section 1.
 //
 // Work decomposition (gfx950: 256 CUs in 8 XCDs, 64-wide waves, 160 KB LDS):
-//   * one 256-thread workgroup (4 waves) per (sequence, head group, split);
-//     a head group is 16 or 32 heads, a split a slice of the top-k list;
+//   * one 256-thread workgroup (4 waves) per (sequence, 16-head group,
+//     split); a split is a slice of the top-k list.  A workgroup needs
+//     under 80 KB of LDS and at most 256 registers per lane, so two run on
+//     every CU and each SIMD interleaves two independent waves;
 //   * prologue: the split's entries are validated, translated through the
 //     page table and compacted into LDS, so -1 padding and out-of-range
 //     entries cost neither a load nor a matrix instruction;
-//   * per tile of 64 selected rows: the raw 22.5 KB are gathered with
-//     coalesced 16-byte loads (prefetched one tile ahead) into LDS; each wave
-//     takes 16 rows, unpacks them in registers straight into the B-operand
-//     layout of v_mfma_f32_16x16x32_f16 (e2m1 -> f16 by the hardware
+//   * per tile of 64 selected rows, each wave takes 16 rows: its lanes load
+//     the 352-byte rows straight into registers in the B-operand layout of
+//     v_mfma_f32_16x16x32_f16 (a lane holds a quarter of one row; the next
+//     tile is in flight meanwhile), unpack them (e2m1 -> f16 by the hardware
 //     converter, times the block scale with a packed f16 multiply; both
-//     exact), scores them against the query held in registers, and stores
-//     the unpacked latent part to LDS once; the online softmax (max and sum
-//     by lane shuffles, per-wave maxima exchanged through LDS) turns scores
-//     into f16 weights; each wave then accumulates the value contraction for
-//     its 128 of the 512 output columns, reading weights and values from LDS
-//     (values through the transposing ds_read_b64_tr_b16);
-//   * all workgroups of one sequence are dispatched to the same XCD so the
-//     head groups re-read each selected row from that XCD's L2;
-//   * when a sequence's top-k list is split over several workgroups, each
-//     writes its partial (m, l, O) to the workspace and a second, small
-//     kernel merges them (a merge inside the first launch would need an
-//     agent-scope release per workgroup, i.e. an L2 writeback, which costs
+//     exact), score them against the query held in registers, and store the
+//     unpacked latent part once into an XOR-swizzled LDS tile;
+//   * softmax: a per-head running max that moves only when a score passes
+//     it by more than kSlack, so after the first tiles the max reductions
+//     and the accumulator rescale are skipped; the decision is shared by the
+//     waves through LDS;
+//   * value contraction: each wave accumulates its 128 of the 512 output
+//     columns over all 64 rows, weights and values from LDS (values through
+//     the transposing ds_read_b64_tr_b16);
+//   * all workgroups of one sequence run on the same XCD (consecutive
+//     workgroup ids go to consecutive XCDs), so the head groups re-read each
+//     selected row from that XCD's L2;
+//   * a split writes its partial (m, l, O) to the workspace and a second,
+//     small kernel merges them (a merge inside the first launch would need
+//     an agent-scope release per workgroup, an L2 writeback, which costs
 //     more than the launch).
 #include "smla_internal.h"
 
@@ -42,15 +47,15 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4_t;
+typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
 
 constexpr int kThreads = 256;
+constexpr int kHeads = 16;                    // heads per workgroup (one MFMA row block)
 constexpr int kTile = 64;                     // selected rows per tile (16 per wave)
-constexpr int kPieces = kTile * kRowBytes / 16;  // 16-byte pieces per tile (1408)
-constexpr int kPiecesPerThread = (kPieces + kThreads - 1) / kThreads;  // 6
-constexpr int kVStride = kLatent + 16;        // f16 elements per LDS value row (1056 B)
 constexpr int kPStride = kTile + 8;           // f16 elements per LDS weight row (144 B)
 constexpr int kKSteps = kDim / 32;            // 18 contraction steps of 32 for the scores
 constexpr float kSlack = 8.0f;                // log2 headroom before the running max moves
+constexpr int kMaxSplits = 16;
 
 __device__ __forceinline__ half8_t join(half2_t a, half2_t b, half2_t c, half2_t d) {
     half8_t r;
@@ -63,8 +68,8 @@ __device__ __forceinline__ half8_t join(half2_t a, half2_t b, half2_t c, half2_t
 // half-row mirror, row mirror); every lane ends with the same value.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
-                                                              0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 CTRL, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float row16_max(float x) {
     x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
@@ -81,16 +86,43 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-// Partial results are streamed out with non-temporal stores so they do not
-// sit dirty in the L2 that the release fence has to write back.
-__device__ __forceinline__ void store_partial(float *p, float v) { __builtin_nontemporal_store(v, p); }
-
 __device__ __forceinline__ _Float16 bf16_to_f16(uint32_t h) {
     return (_Float16)__uint_as_float(h << 16);
 }
 
-template <int HG>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// The part of one row a lane holds: lane group g of a wave owns latent
+// bytes [64g, 64g+64) (dims 128g..128g+127), scale bytes [256+8g, +8) and
+// rope bytes [288+16g, +16) (rope dims 16g..16g+15).
+struct RowPart {
+    uint4 nib[4];
+    uint2 sc;
+    uint4 rope;
+};
+
+__device__ __forceinline__ void load_part(RowPart &p, const uint8_t *__restrict__ cache,
+                                          uint32_t rid, bool valid, int g) {
+    if (valid) {
+        const uint8_t *base = cache + (size_t)rid * kRowBytes;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) p.nib[k] = *reinterpret_cast<const uint4 *>(base + 64 * g + 16 * k);
+        p.sc = *reinterpret_cast<const uint2 *>(base + kScaleOff + 8 * g);
+        p.rope = *reinterpret_cast<const uint4 *>(base + kRopeOff + 16 * g);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) p.nib[k] = make_uint4(0u, 0u, 0u, 0u);
+        p.sc = make_uint2(0u, 0u);
+        p.rope = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// LDS value tile: [64 rows][512 columns] f16, 16-byte chunks of a row stored
+// at chunk ^ (row % 16) so that both the unpacking stores (16 rows, same
+// chunk) and the transposing reads (4 rows x 4 chunks) spread over banks.
+__device__ __forceinline__ int v_index(int row, int col) {
+    return row * kLatent + ((((col >> 3) ^ (row & 15)) << 3) | (col & 7));
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ cache,
                               int64_t num_pages, const int32_t *__restrict__ page_table,
                               int32_t max_pages, const int32_t *__restrict__ seq_lens,
@@ -98,13 +130,11 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                               float scale_log2, float *__restrict__ out, float *__restrict__ lse,
                               float *__restrict__ ws_partials, int32_t batch, int32_t groups,
                               int32_t splits, int32_t per_split) {
-    constexpr int MB = HG / 16;  // 16-head MFMA row blocks
-    __shared__ __attribute__((aligned(16))) uint8_t raw_lds[kTile * kRowBytes];
-    __shared__ __attribute__((aligned(16))) _Float16 v_lds[kTile * kVStride];
-    __shared__ __attribute__((aligned(16))) _Float16 p_lds[HG * kPStride];
+    __shared__ __attribute__((aligned(16))) _Float16 v_lds[kTile * kLatent];
+    __shared__ __attribute__((aligned(16))) _Float16 p_lds[kHeads * kPStride];
     __shared__ uint32_t rowid_lds[kMaxTopk];
-    __shared__ float wmax_lds[4][HG];
-    __shared__ float lsum_lds[4][HG];
+    __shared__ float wmax_lds[4][kHeads];
+    __shared__ float lsum_lds[4][kHeads];
     __shared__ int32_t scan_lds[4];
     __shared__ uint32_t flag_lds[4];
 
@@ -129,7 +159,6 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 
     // ---- prologue: validate, translate, compact the split's entries ----
     const int64_t L = seq_lens[b];
-    const int64_t slots_total = num_pages * kPageRows;
     const int per_thread = (per_split + kThreads - 1) / kThreads;
     uint32_t rid[8];
     int cnt = 0;
@@ -141,10 +170,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
             const int64_t t = topk_idx[(int64_t)b * topk + e];
             if (t >= 0 && t < L && (t >> 6) < max_pages) {
                 const int64_t page = page_table[(int64_t)b * max_pages + (t >> 6)];
-                if (page >= 0 && page < num_pages) {
-                    const int64_t slot = page * kPageRows + (t & 63);
-                    if (slot < slots_total) rid[i] = (uint32_t)slot;
-                }
+                if (page >= 0 && page < num_pages) rid[i] = (uint32_t)(page * kPageRows + (t & 63));
             }
         }
         cnt += rid[i] != 0xFFFFFFFFu;
@@ -174,10 +200,9 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     // A[m = head][k = 8g + i] at score step j holds dim 128g + 8j + i (latent,
     // j < 16) or 512 + 16g + 8(j-16) + i (rope): the same permutation of the
     // 576 dims that the unpacked rows use below.
-    half8_t qa[MB][kKSteps];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int head = hg * HG + mb * 16 + n;
+    half8_t qa[kKSteps];
+    {
+        const int head = hg * kHeads + n;
         const uint16_t *qrow = q + ((int64_t)b * heads + head) * kDim;
 #pragma unroll
         for (int j = 0; j < kKSteps; ++j) {
@@ -186,280 +211,235 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
             const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                qa[mb][j][2 * i] = bf16_to_f16(w4[i] & 0xFFFFu);
-                qa[mb][j][2 * i + 1] = bf16_to_f16(w4[i] >> 16);
+                qa[j][2 * i] = bf16_to_f16(w4[i] & 0xFFFFu);
+                qa[j][2 * i + 1] = bf16_to_f16(w4[i] >> 16);
             }
         }
     }
     __syncthreads();  // rowid_lds complete
 
     const int n_tiles = (n_valid + kTile - 1) / kTile;
+    const int row = wave * 16 + n;  // this lane's row within a tile
 
-    float4_t o[MB][8];
-    float m_run[MB][4], l_run[MB][4];
+    float4_t o[8];
+    float m_run[4], l_run[4];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int nb = 0; nb < 8; ++nb) o[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) o[mb][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) { m_run[mb][r] = -INFINITY; l_run[mb][r] = 0.f; }
-    }
+    for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
 
-    // gather of one tile's raw rows: piece p = tid + 256 i is 16 bytes of row p / 22
-    uint4 pre[kPiecesPerThread];
-    auto gather = [&](int tile) {
-#pragma unroll
-        for (int i = 0; i < kPiecesPerThread; ++i) {
-            const int p = tid + kThreads * i;
-            const int r = p / 22;
-            const int c = p - r * 22;
-            const int idx = tile * kTile + r;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (p < kPieces && idx < n_valid) {
-                const uint8_t *src = cache + (int64_t)rowid_lds[idx] * kRowBytes + c * 16;
-                v = *reinterpret_cast<const uint4 *>(src);
-            }
-            pre[i] = v;
-        }
-    };
-    if (n_tiles > 0) gather(0);
+    RowPart cur, nxt;
+    if (n_tiles > 0) load_part(cur, cache, rowid_lds[min(row, n_valid - 1)], row < n_valid, g);
 
     for (int tile = 0; tile < n_tiles; ++tile) {
-        // (1) publish this tile's raw rows
-#pragma unroll
-        for (int i = 0; i < kPiecesPerThread; ++i) {
-            const int p = tid + kThreads * i;
-            if (p < kPieces) *reinterpret_cast<uint4 *>(raw_lds + p * 16) = pre[i];
-        }
-        __syncthreads();
-        // (2) prefetch the next tile
-        if (tile + 1 < n_tiles) gather(tile + 1);
+        // (1) next tile's rows in flight while this one is processed
+        const int nrow = (tile + 1) * kTile + row;
+        if (tile + 1 < n_tiles)
+            load_part(nxt, cache, rowid_lds[min(nrow, n_valid - 1)], nrow < n_valid, g);
+        // every wave has finished reading the previous tile's values
+        if (tile > 0) __syncthreads();
 
-        // (3) unpack this wave's 16 rows in registers and score them
-        const int row = wave * 16 + n;
-        const uint8_t *rp = raw_lds + row * kRowBytes;
-        uint4 nib[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) nib[k] = *reinterpret_cast<const uint4 *>(rp + 64 * g + 16 * k);
-        const uint2 sc = *reinterpret_cast<const uint2 *>(rp + kScaleOff + 8 * g);
-        const uint4 rope = *reinterpret_cast<const uint4 *>(rp + kRopeOff + 16 * g);
+        // (2) unpack this wave's 16 rows, score them, store the latent part
         half2_t s2[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const uint32_t byte = ((k < 4 ? sc.x : sc.y) >> (8 * (k & 3))) & 0xFFu;
+            const uint32_t byte = ((k < 4 ? cur.sc.x : cur.sc.y) >> (8 * (k & 3))) & 0xFFu;
             s2[k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(byte * 0x0101u, 1.0f, false);
         }
-        float4_t acc[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
-        _Float16 *vrow = v_lds + row * kVStride + 128 * g;
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const uint32_t d = (j & 3) == 0 ? nib[j >> 2].x : (j & 3) == 1 ? nib[j >> 2].y
-                             : (j & 3) == 2 ? nib[j >> 2].z : nib[j >> 2].w;
+            const uint4 nq = cur.nib[j >> 2];
+            const uint32_t d = (j & 3) == 0 ? nq.x : (j & 3) == 1 ? nq.y : (j & 3) == 2 ? nq.z : nq.w;
             const half2_t sv = s2[j >> 1];
             const half2_t e0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * sv;
             const half2_t e1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * sv;
             const half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * sv;
             const half2_t e3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * sv;
             const half8_t kb = join(e0, e1, e2, e3);
-            *reinterpret_cast<half8_t *>(vrow + 8 * j) = kb;
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[mb][j], kb, acc[mb], 0, 0, 0);
+            *reinterpret_cast<half8_t *>(v_lds + v_index(row, 128 * g + 8 * j)) = kb;
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j], kb, acc, 0, 0, 0);
         }
 #pragma unroll
         for (int j = 16; j < 18; ++j) {
-            const uint32_t d0 = (j == 16) ? rope.x : rope.z;
-            const uint32_t d1 = (j == 16) ? rope.y : rope.w;
+            const uint32_t d0 = (j == 16) ? cur.rope.x : cur.rope.z;
+            const uint32_t d1 = (j == 16) ? cur.rope.y : cur.rope.w;
             const half8_t kb = join(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false),
                                     __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true),
                                     __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false),
                                     __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true));
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[mb][j], kb, acc[mb], 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j], kb, acc, 0, 0, 0);
         }
 
-        // (4) scores in log2 units; decide whether any head's running max
-        // must move.  The running max only moves when a score exceeds it by
-        // more than kSlack (weights then stay <= 2^kSlack, fine in f16), so
-        // after the first tiles the max, the rescale and their cross-lane
-        // reductions are skipped.  The decision is shared by all waves.
+        // (3) scores in log2 units; does any head's running max move?  It
+        // moves only when a score passes it by more than kSlack (weights stay
+        // <= 2^kSlack, fine in f16), so after the first tiles the max, the
+        // rescale and their cross-lane reductions are skipped.  The decision
+        // is shared by all waves.
         const bool valid = tile * kTile + row < n_valid;
-        float x[MB][4];
+        float x[4];
         bool over = false;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                x[mb][r] = valid ? acc[mb][r] * scale_log2 : -INFINITY;
-                over |= x[mb][r] > m_run[mb][r] + kSlack;
-            }
+        for (int r = 0; r < 4; ++r) {
+            x[r] = valid ? acc[r] * scale_log2 : -INFINITY;
+            over |= x[r] > m_run[r] + kSlack;
+        }
         const uint64_t ballot = __ballot(over);
         if (lane == 0) flag_lds[wave] = ballot != 0;
         __syncthreads();
-        const bool move = (flag_lds[0] | flag_lds[1] | flag_lds[2] | flag_lds[3]) != 0;
-        if (move) {
+        if ((flag_lds[0] | flag_lds[1] | flag_lds[2] | flag_lds[3]) != 0) {
             // exact tile maxima per head, exchanged through LDS
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float mx = row16_max(x[mb][r]);
-                    if (n == 0) wmax_lds[wave][mb * 16 + 4 * g + r] = mx;
-                }
+            for (int r = 0; r < 4; ++r) {
+                const float mx = row16_max(x[r]);
+                if (n == 0) wmax_lds[wave][4 * g + r] = mx;
+            }
             __syncthreads();
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+            for (int r = 0; r < 4; ++r) {
+                const int h = 4 * g + r;
+                const float mt = fmaxf(fmaxf(wmax_lds[0][h], wmax_lds[1][h]),
+                                       fmaxf(wmax_lds[2][h], wmax_lds[3][h]));
+                const float m_new = fmaxf(m_run[r], mt);
+                // m_new = -inf only while nothing valid was seen: keep zeros
+                const float alpha =
+                    (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[r] - m_new);
+                m_run[r] = m_new;
+                l_run[r] *= alpha;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int h = mb * 16 + 4 * g + r;
-                    const float mt = fmaxf(fmaxf(wmax_lds[0][h], wmax_lds[1][h]),
-                                           fmaxf(wmax_lds[2][h], wmax_lds[3][h]));
-                    const float m_new = fmaxf(m_run[mb][r], mt);
-                    // m_new = -inf only while nothing valid was seen: keep zeros
-                    const float alpha = (m_new == -INFINITY)
-                                            ? 1.0f
-                                            : __builtin_amdgcn_exp2f(m_run[mb][r] - m_new);
-                    m_run[mb][r] = m_new;
-                    l_run[mb][r] *= alpha;
-#pragma unroll
-                    for (int nb = 0; nb < 8; ++nb) o[mb][nb][r] *= alpha;
-                }
+                for (int nb = 0; nb < 8; ++nb) o[nb][r] *= alpha;
+            }
         }
 
-        // (5) f16 weights to LDS; each lane keeps its own share of the sum
+        // (4) f16 weights to LDS; each lane keeps its own share of the sum
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int h = mb * 16 + 4 * g + r;
-                const float p = (m_run[mb][r] == -INFINITY)
-                                    ? 0.0f
-                                    : __builtin_amdgcn_exp2f(x[mb][r] - m_run[mb][r]);
-                const _Float16 ph = (_Float16)p;
-                p_lds[h * kPStride + row] = ph;
-                l_run[mb][r] += (float)ph;  // the normaliser sums the weights actually used
-            }
+        for (int r = 0; r < 4; ++r) {
+            const float p =
+                (m_run[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[r] - m_run[r]);
+            const _Float16 ph = (_Float16)p;
+            p_lds[(4 * g + r) * kPStride + row] = ph;
+            l_run[r] += (float)ph;  // the normaliser sums the weights actually used
+        }
         __syncthreads();
 
-        // (6) value contraction: this wave's 128 output columns, all 64 rows
-        typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+        // (5) value contraction: this wave's 128 output columns, all 64 rows
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            half8_t pa[MB];
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                pa[mb] = *reinterpret_cast<const half8_t *>(p_lds + (mb * 16 + n) * kPStride +
-                                                            32 * ks + 8 * g);
+            const half8_t pa = *reinterpret_cast<const half8_t *>(p_lds + n * kPStride + 32 * ks + 8 * g);
             const int vr = 32 * ks + 8 * g + (n >> 2);
             fp16x4_t vlo[8], vhi[8];
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
                 const int col = 128 * wave + 16 * nb + 4 * (n & 3);
                 vlo[nb] = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)(
-                    (__attribute__((address_space(3))) _Float16 *)(v_lds + vr * kVStride + col)));
+                    (__attribute__((address_space(3))) _Float16 *)(v_lds + v_index(vr, col))));
                 vhi[nb] = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)(
-                    (__attribute__((address_space(3))) _Float16 *)(v_lds + (vr + 4) * kVStride + col)));
+                    (__attribute__((address_space(3))) _Float16 *)(v_lds + v_index(vr + 4, col))));
             }
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
                 half8_t vb;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) { vb[i] = (_Float16)vlo[nb][i]; vb[4 + i] = (_Float16)vhi[nb][i]; }
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[mb], vb, o[mb][nb], 0, 0, 0);
+                o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[nb], 0, 0, 0);
             }
         }
+        cur = nxt;
     }
 
     // ---- epilogue: combine the lanes' and the waves' shares of the sums ----
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float ls = row16_sum(l_run[mb][r]);
-            if (n == 0) lsum_lds[wave][mb * 16 + 4 * g + r] = ls;
-        }
+    for (int r = 0; r < 4; ++r) {
+        const float ls = row16_sum(l_run[r]);
+        if (n == 0) lsum_lds[wave][4 * g + r] = ls;
+    }
     __syncthreads();
-    float l_tot[MB][4];
+    float l_tot[4];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int r = 0; r < 4; ++r) {
+        const int h = 4 * g + r;
+        l_tot[r] = lsum_lds[0][h] + lsum_lds[1][h] + lsum_lds[2][h] + lsum_lds[3][h];
+    }
+
+    if (splits == 1) {
+        const float ln2 = 0.69314718055994530942f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int h = mb * 16 + 4 * g + r;
-            l_tot[mb][r] = lsum_lds[0][h] + lsum_lds[1][h] + lsum_lds[2][h] + lsum_lds[3][h];
+            const int head = hg * kHeads + 4 * g + r;
+            const float inv = l_tot[r] > 0.f ? 1.0f / l_tot[r] : 0.f;
+            float *orow = out + ((int64_t)b * heads + head) * kLatent + 128 * wave + n;
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) orow[16 * nb] = o[nb][r] * inv;
+            if (wave == 0 && n == 0)
+                lse[(int64_t)b * heads + head] =
+                    l_tot[r] > 0.f ? (m_run[r] + log2f(l_tot[r])) * ln2 : -INFINITY;
         }
-
-    const float ln2 = 0.69314718055994530942f;
-    if (splits == 1) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int head = hg * HG + mb * 16 + 4 * g + r;
-                const float inv = l_tot[mb][r] > 0.f ? 1.0f / l_tot[mb][r] : 0.f;
-                float *orow = out + ((int64_t)b * heads + head) * kLatent + 128 * wave + n;
-#pragma unroll
-                for (int nb = 0; nb < 8; ++nb) orow[16 * nb] = o[mb][nb][r] * inv;
-                if (wave == 0 && n == 0)
-                    lse[(int64_t)b * heads + head] =
-                        l_tot[mb][r] > 0.f ? (m_run[mb][r] + log2f(l_tot[mb][r])) * ln2 : -INFINITY;
-            }
         return;
     }
 
     // ---- split: publish the partial; the merge kernel combines them ----
-    // Partial layout per (unit, split): O[HG][512] unnormalised, then m[HG]
-    // (running max, log2 units) and l[HG] (sum of weights).
-    const size_t pfl = (size_t)HG * kLatent + 2 * HG;
+    // Partial layout per (unit, split): O[16][512] unnormalised, then m[16]
+    // (running max, log2 units) and l[16] (sum of weights).
+    const size_t pfl = (size_t)kHeads * kLatent + 2 * kHeads;
     float *part = ws_partials + ((size_t)unit * splits + split) * pfl;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int r = 0; r < 4; ++r) {
+        const int h = 4 * g + r;
+        float *prow = part + (size_t)h * kLatent + 128 * wave + n;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int h = mb * 16 + 4 * g + r;
-            float *prow = part + (size_t)h * kLatent + 128 * wave + n;
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb) prow[16 * nb] = o[mb][nb][r];
-            if (wave == 0 && n == 0) {
-                part[(size_t)HG * kLatent + h] = m_run[mb][r];
-                part[(size_t)HG * kLatent + HG + h] = l_tot[mb][r];
-            }
+        for (int nb = 0; nb < 8; ++nb) prow[16 * nb] = o[nb][r];
+        if (wave == 0 && n == 0) {
+            part[(size_t)kHeads * kLatent + h] = m_run[r];
+            part[(size_t)kHeads * kLatent + kHeads + h] = l_tot[r];
         }
+    }
 }
 
-// Merge of the splits' partials: one thread per (unit, head, 4 columns), the
-// splits combined in split order (fixed, hence deterministic):
+// Merge of the splits' partials: one thread per (unit, head, 4 columns); all
+// splits' loads are issued up front, then combined in split order (fixed,
+// hence deterministic):
 //   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,  O = sum_s 2^(m_s - M) O_s / L.
 __global__ __launch_bounds__(256) void merge_splits_kernel(
     const float *__restrict__ ws_partials, float *__restrict__ out, float *__restrict__ lse,
-    int32_t heads, int32_t hg_size, int32_t groups, int32_t splits, int32_t units) {
+    int32_t heads, int32_t groups, int32_t splits, int32_t units) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)units * hg_size * (kLatent / 4);
+    const int64_t total = (int64_t)units * kHeads * (kLatent / 4);
     if (idx >= total) return;
     const int c4 = (int)(idx % (kLatent / 4));
-    const int h = (int)((idx / (kLatent / 4)) % hg_size);
-    const int unit = (int)(idx / ((int64_t)(kLatent / 4) * hg_size));
-    const size_t pfl = (size_t)hg_size * kLatent + 2 * hg_size;
+    const int h = (int)((idx / (kLatent / 4)) % kHeads);
+    const int unit = (int)(idx / ((int64_t)(kLatent / 4) * kHeads));
+    const size_t pfl = (size_t)kHeads * kLatent + 2 * kHeads;
     const float *base = ws_partials + (size_t)unit * splits * pfl;
+    float ms[kMaxSplits], ls[kMaxSplits];
+    float4_t os[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+        if (s < splits) {
+            const float *ps = base + s * pfl;
+            ms[s] = ps[(size_t)kHeads * kLatent + h];
+            ls[s] = ps[(size_t)kHeads * kLatent + kHeads + h];
+            os[s] = *reinterpret_cast<const float4_t *>(ps + (size_t)h * kLatent + 4 * c4);
+        } else {
+            ms[s] = -INFINITY;
+            ls[s] = 0.f;
+            os[s] = float4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
     float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, base[s * pfl + (size_t)hg_size * kLatent + h]);
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, ms[s]);
     float L = 0.f;
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
-        for (int s = 0; s < splits; ++s) {
-            const float *ps = base + s * pfl;
-            const float w = __builtin_amdgcn_exp2f(ps[(size_t)hg_size * kLatent + h] - M);
-            L += w * ps[(size_t)hg_size * kLatent + hg_size + h];
-            const float4_t v = *reinterpret_cast<const float4_t *>(ps + (size_t)h * kLatent + 4 * c4);
-            acc += w * v;
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s) {
+            const float w = __builtin_amdgcn_exp2f(ms[s] - M);
+            L += w * ls[s];
+            acc += w * os[s];
         }
     }
     const int b = unit / groups;
-    const int head = (unit % groups) * hg_size + h;
+    const int head = (unit % groups) * kHeads + h;
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     *reinterpret_cast<float4_t *>(out + ((int64_t)b * heads + head) * kLatent + 4 * c4) = acc * inv;
     if (c4 == 0)
@@ -471,21 +451,18 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(
 
 DecodePlan plan_decode(int batch, int heads, int topk) {
     DecodePlan p;
-    // 16 heads per workgroup: one MFMA row block, the query and the
-    // accumulators fit in registers with room for the pipeline, and more
-    // workgroups per sequence share each selected row through the XCD's L2.
-    p.heads_per_group = 16;
-    p.groups = heads / p.heads_per_group;
+    p.heads_per_group = kHeads;
+    p.groups = heads / kHeads;
     const int units = batch * p.groups;
-    const int target = 256;  // one workgroup per CU
+    const int target = 512;  // two workgroups per CU
     int s = (target + units - 1) / units;
     const int max_s = (topk + kTile - 1) / kTile;
     s = s < 1 ? 1 : s;
     s = s > max_s ? max_s : s;
-    s = s > 16 ? 16 : s;
+    s = s > kMaxSplits ? kMaxSplits : s;
     p.splits = s;
     p.per_split = (topk + s - 1) / s;
-    p.partial_floats = (size_t)p.heads_per_group * kLatent + 2 * p.heads_per_group;
+    p.partial_floats = (size_t)kHeads * kLatent + 2 * kHeads;
     if (s == 1) {
         p.workspace_bytes = 0;
     } else {
@@ -504,24 +481,16 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
     const int blocks = ((batch + 7) / 8) * 8 * plan.groups * plan.splits;
     float *partials = plan.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     const float scale_log2 = (float)((double)scale * 1.4426950408889634074);
-    if (plan.heads_per_group == 32) {
-        hipLaunchKernelGGL(sparse_mla_decode_kernel<32>, dim3(blocks), dim3(kThreads), 0, stream,
-                           q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,
-                           topk, scale_log2, out, lse, partials, batch, plan.groups, plan.splits,
-                           plan.per_split);
-    } else {
-        hipLaunchKernelGGL(sparse_mla_decode_kernel<16>, dim3(blocks), dim3(kThreads), 0, stream,
-                           q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,
-                           topk, scale_log2, out, lse, partials, batch, plan.groups, plan.splits,
-                           plan.per_split);
-    }
+    hipLaunchKernelGGL(sparse_mla_decode_kernel, dim3(blocks), dim3(kThreads), 0, stream, q, cache,
+                       num_pages, page_table, max_pages, seq_lens, topk_idx, heads, topk,
+                       scale_log2, out, lse, partials, batch, plan.groups, plan.splits,
+                       plan.per_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
     const int units = batch * plan.groups;
-    const int64_t threads = (int64_t)units * plan.heads_per_group * (kLatent / 4);
+    const int64_t threads = (int64_t)units * kHeads * (kLatent / 4);
     hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       stream, partials, out, lse, heads, plan.heads_per_group, plan.groups,
-                       plan.splits, units);
+                       stream, partials, out, lse, heads, plan.groups, plan.splits, units);
     return hipGetLastError();
 }
 
