@@ -38,12 +38,14 @@ def test_workspace_sizes():
     assert smla.decode_workspace_bytes(0, 64, 2048) == 0
     assert smla.decode_workspace_bytes(4, 32, 2048) == 0          # heads unsupported
     assert smla.decode_workspace_bytes(4, 64, 4096) == 0          # topk too large
-    # batch 64 x 64 heads: 256 workgroups of 16 heads, no split, no workspace
-    assert smla.decode_workspace_bytes(64, 64, 2048) == 0
-    # batch 1 x 64 heads: 4 head groups x 16 splits of 16-head partials
+    # one sequence with 64 heads is split over many workgroups: partials of
+    # at least 16 heads x 512 columns each, for more than one split
     ws = smla.decode_workspace_bytes(1, 64, 2048)
-    assert ws >= 4 * 16 * (16 * 512 + 32) * 4
+    assert ws >= 2 * (16 * 512 + 32) * 4
     assert ws % 256 == 0
+    assert smla.decode_workspace_bytes(64, 64, 2048) % 256 == 0
+    # a single 64-entry list cannot be split
+    assert smla.decode_workspace_bytes(1, 16, 64) == 0
 
 
 FAKE = 0x10000  # never dereferenced: every call below fails host-side validation
