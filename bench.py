@@ -33,8 +33,8 @@ APPEND_BYTES_PER_ROW = 576 * 2 + ROW_BYTES     # BF16 row read + NVFP4 row writt
 FLOPS_PER_HEAD_ROW = 2 * 576 + 2 * 512         # score + value contraction
 CACHE_BYTES_MALL = 256 << 20
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "sparse_mla_decode_amd", "csrc", "sparse_mla_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.txt")
+CALIB_FLOATS = 64 << 20          # calibration kernel: y = -x over 256 MiB of fp32
 
 
 def log(msg):
@@ -51,17 +51,79 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, or None
-    when the kernel source changed since they were taken."""
+    """HBM bytes per decode call from committed rocprofv3 counter runs, or None
+    when the kernel source changed since they were taken.  The file holds one
+    line per workload: `<workload> <source hash> <bytes per call> ...`."""
     try:
         with open(TRAFFIC_FILE) as f:
-            d = json.load(f)
-    except (OSError, ValueError):
+            lines = f.read().splitlines()
+    except OSError:
         return None
-    rec = d.get(workload)
-    if not rec or rec.get("source_hash") != kernel_source_hash():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    for ln in lines:
+        parts = ln.split()
+        if len(parts) >= 3 and parts[0] == workload and not ln.startswith("#"):
+            if parts[1] != kernel_source_hash():
+                return None
+            return int(parts[2])
+    return None
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def summarize_kernel_stats(d):
+    """Text summary of a rocprofv3 --kernel-trace --stats directory: the
+    library's kernels (and the total of one decode call)."""
+    rows = _csv_rows(d, "kernel_stats.csv")
+    out = ["%-60s %8s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
+    for r in rows:
+        name = r["Name"]
+        if "smla" not in name:
+            continue
+        short = name.replace("smla::(anonymous namespace)::", "").split("(")[0]
+        out.append("%-60s %8s %12.3f %12.3f %12.3f" % (
+            short[:60], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3))
+    return "\n".join(out)
+
+
+def summarize_counters(fetch_dir, write_dir, workload):
+    """HBM bytes per decode call from two rocprofv3 --pmc runs (FETCH_SIZE,
+    then WRITE_SIZE, both in KiB per dispatch), each scaled by what the same
+    counter reads for the calibration kernel (y = -x over 256 MiB fp32: reads
+    256 MiB, writes 256 MiB)."""
+    res = {}
+    for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        per = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        calib = [v for k, vs in per.items() if "neg" in k for v in vs]
+        dec = [v for k, vs in per.items() if "sparse_mla_decode_kernel" in k for v in vs]
+        mrg = [v for k, vs in per.items() if "merge_splits_kernel" in k for v in vs]
+        if not calib or not dec:
+            raise SystemExit("missing calibration or decode dispatches in %s" % d)
+        kib_true = CALIB_FLOATS * 4 / 1024.0
+        factor = kib_true / (sum(calib) / len(calib))
+        dec_kib = sum(dec) / len(dec)
+        mrg_kib = sum(mrg) / len(mrg) if mrg else 0.0
+        res[counter] = (factor, dec_kib, mrg_kib, len(dec))
+    fb = (res["FETCH_SIZE"][1] + res["FETCH_SIZE"][2]) * res["FETCH_SIZE"][0] * 1024
+    wb = (res["WRITE_SIZE"][1] + res["WRITE_SIZE"][2]) * res["WRITE_SIZE"][0] * 1024
+    lines = ["# counter  factor  decode_KiB/dispatch  merge_KiB/dispatch  dispatches"]
+    for c, (f, dk, mk, n) in res.items():
+        lines.append("# %-10s %.4f %14.1f %14.1f %6d" % (c, f, dk, mk, n))
+    lines.append("# workload  source_hash  hbm_bytes_per_call  fetch_bytes  write_bytes")
+    lines.append("%s %s %d %d %d" % (workload, kernel_source_hash(), int(fb + wb), int(fb), int(wb)))
+    return "\n".join(lines)
 
 
 def cpu_baseline(w, seed, lens, tk_np, qbits, budget_s, dev):
@@ -110,8 +172,19 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="run one 256 MiB device copy first (counter calibration)")
+                    help="run y = -x over 256 MiB first (HBM counter calibration)")
+    ap.add_argument("--summarize-kernel-stats", metavar="DIR",
+                    help="print a summary of a rocprofv3 --kernel-trace --stats directory")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print HBM bytes per decode call from FETCH_SIZE / WRITE_SIZE runs")
     args = ap.parse_args()
+
+    if args.summarize_kernel_stats:
+        print(summarize_kernel_stats(args.summarize_kernel_stats))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters, args.workload))
+        return
 
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -131,9 +204,10 @@ def main():
     log("workload %s: %s; cache %d pages (%.2f GB)" % (w.name, w.desc, num_pages,
                                                        num_pages * 22528 / 1e9))
     if args.calibrate_copy:
-        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        a = torch.ones(CALIB_FLOATS, dtype=torch.float32, device=dev)
         b_ = torch.empty_like(a)
-        b_.copy_(a)
+        torch.cuda.synchronize()
+        torch.neg(a, out=b_)
         torch.cuda.synchronize()
         del a, b_
 
