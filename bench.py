@@ -82,12 +82,19 @@ def summarize_kernel_stats(d):
     """Text summary of a rocprofv3 --kernel-trace --stats directory: the
     library's kernels (and the total of one decode call)."""
     rows = _csv_rows(d, "kernel_stats.csv")
+    import re
     out = ["%-60s %8s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
     for r in rows:
         name = r["Name"]
         if "smla" not in name:
             continue
-        short = name.replace("smla::(anonymous namespace)::", "").split("(")[0]
+        # demangled (smla::(anonymous namespace)::k<2>(...)) or mangled
+        # (_ZN4smla12_GLOBAL__N_11kILi2EEEv...) names -> k or k<2>
+        m = re.search(r"(kv_quant_append_kernel|sparse_mla_decode_kernel|merge_splits_kernel)"
+                      r"(?:ILi(\d+)E|<(\d+)>)?", name)
+        if not m:
+            continue
+        short = m.group(1) + ("<%s>" % (m.group(2) or m.group(3)) if (m.group(2) or m.group(3)) else "")
         out.append("%-60s %8s %12.3f %12.3f %12.3f" % (
             short[:60], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3))

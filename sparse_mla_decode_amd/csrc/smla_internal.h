@@ -28,7 +28,7 @@ struct DecodePlan {
     int groups;           // heads / heads_per_group
     int splits;           // workgroups sharing one (sequence, head group)
     int per_split;        // top-k entries each split scans
-    size_t partial_floats;  // floats per partial result
+    size_t partial_bytes; // bytes of one split's partial result
     size_t workspace_bytes;
 };
 

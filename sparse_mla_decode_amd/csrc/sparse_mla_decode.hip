@@ -5,39 +5,40 @@
 // KV-cache problem", section "A kernel that reads four bits directly" (load
 // the selected 352-byte rows, unpack on chip, score, softmax and blend; -1
 // entries carry no data) and Prime Intellect's launch post, native-kernel
-// paragraph (FP16 operands, FP32 accumulation, partial results of the blocks
-// sharing a query merged after the split).  Every selected row serves all
-// heads of the query: "GLM-5.3 PCP/DCP long-context on H200", section 1.
+// paragraph (FP16 operands, FP32 accumulation; the blocks sharing a query
+// merge their partial results).  Every selected row serves all heads of the
+// query: "GLM-5.3 PCP/DCP long-context on H200", section 1.
 //
 // Work decomposition (gfx950: 256 CUs in 8 XCDs, 64-wide waves, 160 KB LDS):
-//   * one 256-thread workgroup (4 waves) per (sequence, 16-head group,
-//     split); a split is a slice of the top-k list.  A workgroup needs
-//     under 80 KB of LDS and at most 256 registers per lane, so two run on
-//     every CU and each SIMD interleaves two independent waves;
+//   * one 256-thread workgroup (one wave per SIMD, up to 512 registers per
+//     lane) per (sequence, head group, split) and CU; a head group is 32
+//     heads (16 when a query has only 16), a split a slice of the top-k list;
 //   * prologue: the split's entries are validated, translated through the
 //     page table and compacted into LDS, so -1 padding and out-of-range
 //     entries cost neither a load nor a matrix instruction;
-//   * per tile of 64 selected rows, each wave takes 16 rows: its lanes load
-//     the 352-byte rows straight into registers in the B-operand layout of
-//     v_mfma_f32_16x16x32_f16 (a lane holds a quarter of one row; the next
-//     tile is in flight meanwhile), unpack them (e2m1 -> f16 by the hardware
-//     converter, times the block scale with a packed f16 multiply; both
-//     exact), score them against the query held in registers, and store the
-//     unpacked latent part once into an XOR-swizzled LDS tile;
-//   * softmax: a per-head running max that moves only when a score passes
-//     it by more than kSlack, so after the first tiles the max reductions
-//     and the accumulator rescale are skipped; the decision is shared by the
-//     waves through LDS;
-//   * value contraction: each wave accumulates its 128 of the 512 output
-//     columns over all 64 rows, weights and values from LDS (values through
-//     the transposing ds_read_b64_tr_b16);
+//   * the selected rows travel HBM -> LDS still packed (352 bytes each) by
+//     direct-to-LDS 16-byte loads: 64 rows = 22 wave-wide loads of
+//     consecutive bytes, four tiles in flight in a ring of five, so the
+//     gathers are coalesced and deep;
+//   * scores: each wave takes 16 rows of the tile; a lane reads the packed
+//     bytes of one row, unpacks them in registers (e2m1 -> f16 by the
+//     hardware converter, times the block scale with a packed f16 multiply,
+//     rope bytes E4M3 -> f16; all exact) and feeds MFMA 16x16x32 f16 against
+//     the query held in registers: one unpack serves every head of the group;
+//   * online softmax: the running max moves only when a score passes it by
+//     more than kSlack (log2 units), so normally no max reduction, rescale or
+//     extra barrier is needed;
+//   * values: each wave owns 128 of the 512 output columns; the transposing
+//     4-bit LDS read (ds_read_b64_tr_b4) hands a lane 16 rows of one column
+//     still packed, which are unpacked and scaled (scales from a per-tile
+//     transposed f16 table) and fed to MFMA 32x32x16 f16;
 //   * all workgroups of one sequence run on the same XCD (consecutive
-//     workgroup ids go to consecutive XCDs), so the head groups re-read each
-//     selected row from that XCD's L2;
-//   * a split writes its partial (m, l, O) to the workspace and a second,
-//     small kernel merges them (a merge inside the first launch would need
-//     an agent-scope release per workgroup, an L2 writeback, which costs
-//     more than the launch).
+//     workgroup ids go to consecutive XCDs), so head groups re-read shared
+//     rows from that XCD's L2;
+//   * a split writes its normalised partial output (f16) with its running
+//     max and sum to the workspace, and a second small kernel merges them (a
+//     merge inside the first launch would need an agent-scope release per
+//     workgroup, an L2 writeback, which costs more than the launch).
 #include "smla_internal.h"
 
 namespace smla {
@@ -46,16 +47,23 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4_t;
-typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef int int2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) int2_t lds_int2_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kThreads = 256;
-constexpr int kHeads = 16;                    // heads per workgroup (one MFMA row block)
-constexpr int kTile = 64;                     // selected rows per tile (16 per wave)
-constexpr int kPStride = kTile + 8;           // f16 elements per LDS weight row (144 B)
-constexpr int kKSteps = kDim / 32;            // 18 contraction steps of 32 for the scores
-constexpr float kSlack = 8.0f;                // log2 headroom before the running max moves
+constexpr int kThreads = 512;                   // 4 score waves + 4 value waves, two per SIMD
+constexpr int kTile = 64;                       // selected rows per tile (16 per wave)
+constexpr int kNBuf = 5;                        // ring of packed tiles in LDS (3 in flight)
+constexpr int kTileBytes = kTile * kRowBytes;   // 22,528
+constexpr int kDmaPerTile = kTileBytes / 1024;  // wave-wide 16-byte loads per tile (22)
+constexpr int kPStride = kTile + 8;             // f16 per softmax-weight row (144 B)
+constexpr int kSStride = kTile + 8;             // f16 per scale-table row (144 B)
+constexpr int kKSteps = kDim / 32;              // 18 score steps of 32
+constexpr float kSlack = 8.0f;                  // log2 headroom before the running max moves
 constexpr int kMaxSplits = 16;
+static_assert(kTileBytes % 1024 == 0, "a tile must be whole wave-wide loads");
+static_assert(kDmaPerTile > 16 && kDmaPerTile <= 24, "2 or 3 loads per wave per tile");
 
 __device__ __forceinline__ half8_t join(half2_t a, half2_t b, half2_t c, half2_t d) {
     half8_t r;
@@ -90,59 +98,78 @@ __device__ __forceinline__ _Float16 bf16_to_f16(uint32_t h) {
     return (_Float16)__uint_as_float(h << 16);
 }
 
-// The part of one row a lane holds: lane group g of a wave owns latent
-// bytes [64g, 64g+64) (dims 128g..128g+127), scale bytes [256+8g, +8) and
-// rope bytes [288+16g, +16) (rope dims 16g..16g+15).
-struct RowPart {
-    uint4 nib[4];
-    uint2 sc;
-    uint4 rope;
-};
+// e2m1 pair (byte SEL of w) -> f16 pair, exact
+template <int SEL>
+__device__ __forceinline__ half2_t fp4x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+// E4M3 pair (bytes 0,1 if HI is false, else 2,3 of w) -> f16 pair, exact
+template <bool HI>
+__device__ __forceinline__ half2_t fp8x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
 
-__device__ __forceinline__ void load_part(RowPart &p, const uint8_t *__restrict__ cache,
-                                          uint32_t rid, bool valid, int g) {
-    if (valid) {
-        const uint8_t *base = cache + (size_t)rid * kRowBytes;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) p.nib[k] = *reinterpret_cast<const uint4 *>(base + 64 * g + 16 * k);
-        p.sc = *reinterpret_cast<const uint2 *>(base + kScaleOff + 8 * g);
-        p.rope = *reinterpret_cast<const uint4 *>(base + kRopeOff + 16 * g);
-    } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) p.nib[k] = make_uint4(0u, 0u, 0u, 0u);
-        p.sc = make_uint2(0u, 0u);
-        p.rope = make_uint4(0u, 0u, 0u, 0u);
+// One wave-wide direct-to-LDS load: lane l's 16 bytes at gptr go to LDS
+// byte lds_addr + 16 l.  Written as inline assembly so that the compiler does
+// not insert its own (full) waits for it before later LDS reads; the tile
+// ring waits for these loads explicitly with wait_vmcnt.
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+// Wait until at most N of this wave's memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_n() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most n of this wave's memory loads are outstanding (n is
+// wave-uniform and one of the counts the tile ring produces).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (n) {
+#define SMLA_WAIT(N) case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
+        SMLA_WAIT(0) SMLA_WAIT(1) SMLA_WAIT(2) SMLA_WAIT(3) SMLA_WAIT(4) SMLA_WAIT(5)
+        SMLA_WAIT(6) SMLA_WAIT(7) SMLA_WAIT(8) SMLA_WAIT(9) SMLA_WAIT(10) SMLA_WAIT(11)
+        SMLA_WAIT(12) SMLA_WAIT(13) SMLA_WAIT(14) SMLA_WAIT(15) SMLA_WAIT(16) SMLA_WAIT(17)
+        SMLA_WAIT(18) SMLA_WAIT(19) SMLA_WAIT(20) SMLA_WAIT(21) SMLA_WAIT(22) SMLA_WAIT(23)
+        SMLA_WAIT(24)
+#undef SMLA_WAIT
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     }
 }
 
-// LDS value tile: [64 rows][512 columns] f16, 16-byte chunks of a row stored
-// at chunk ^ (row % 16) so that both the unpacking stores (16 rows, same
-// chunk) and the transposing reads (4 rows x 4 chunks) spread over banks.
-__device__ __forceinline__ int v_index(int row, int col) {
-    return row * kLatent + ((((col >> 3) ^ (row & 15)) << 3) | (col & 7));
-}
-
+template <int MB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ cache,
                               int64_t num_pages, const int32_t *__restrict__ page_table,
                               int32_t max_pages, const int32_t *__restrict__ seq_lens,
                               const int32_t *__restrict__ topk_idx, int32_t heads, int32_t topk,
                               float scale_log2, float *__restrict__ out, float *__restrict__ lse,
-                              float *__restrict__ ws_partials, int32_t batch, int32_t groups,
-                              int32_t splits, int32_t per_split) {
-    __shared__ __attribute__((aligned(16))) _Float16 v_lds[kTile * kLatent];
-    __shared__ __attribute__((aligned(16))) _Float16 p_lds[kHeads * kPStride];
+                              _Float16 *__restrict__ part_o, float *__restrict__ part_ml,
+                              int32_t batch, int32_t groups, int32_t splits, int32_t per_split) {
+    constexpr int HG = 16 * MB;  // heads of this workgroup
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kNBuf * kTileBytes];
+    __shared__ __attribute__((aligned(16))) _Float16 p_lds[2][32 * kPStride];
+    __shared__ __attribute__((aligned(16))) _Float16 st_lds[2][32 * kSStride];
     __shared__ uint32_t rowid_lds[kMaxTopk];
-    __shared__ float wmax_lds[4][kHeads];
-    __shared__ float lsum_lds[4][kHeads];
-    __shared__ int32_t scan_lds[4];
-    __shared__ uint32_t flag_lds[4];
+    __shared__ float red_lds[2][4][32];   // tile maxima of the score waves that flagged
+    __shared__ float alpha_lds[2][32];    // rescale factors when the running max moved
+    __shared__ float sum_lds[4][32];
+    __shared__ float m_lds[32];
+    __shared__ int32_t scan_lds[8];
+    __shared__ uint32_t flag_lds[2][4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int n = lane & 15;   // row (scores) / column (values) within a 16-block
-    const int g = lane >> 4;   // 8-element k group
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int sw = wave & 3;    // score wave: rows 16 sw ..; value wave: columns 128 sw ..
+    const int n = lane & 15;    // score MFMA: row within the wave's 16 / head within 16
+    const int g = lane >> 4;    // score MFMA: 8-element k group
+    const int n32 = lane & 31;  // value MFMA: column within a 32-column block / head
+    const int g2 = lane >> 5;   // value MFMA: 8-element k group
 
     // ---- which (sequence, head group, split): consecutive workgroups go to
     // consecutive XCDs, so all workgroups of sequence b share XCD b % 8 ----
@@ -158,291 +185,463 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     const int e_end = min(topk, e_begin + per_split);
 
     // ---- prologue: validate, translate, compact the split's entries ----
+    // All index loads are issued before any is used (two round trips); an
+    // entry outside its range reads a harmless in-range word instead.
     const int64_t L = seq_lens[b];
-    const int per_thread = (per_split + kThreads - 1) / kThreads;
-    uint32_t rid[8];
-    int cnt = 0;
+    const int per_thread = (per_split + kThreads - 1) / kThreads;  // <= 4
+    int32_t tv[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        rid[i] = 0xFFFFFFFFu;
+    for (int i = 0; i < 4; ++i) {
         const int e = e_begin + tid * per_thread + i;
-        if (i < per_thread && e < e_end) {
-            const int64_t t = topk_idx[(int64_t)b * topk + e];
-            if (t >= 0 && t < L && (t >> 6) < max_pages) {
-                const int64_t page = page_table[(int64_t)b * max_pages + (t >> 6)];
-                if (page >= 0 && page < num_pages) rid[i] = (uint32_t)(page * kPageRows + (t & 63));
-            }
-        }
-        cnt += rid[i] != 0xFFFFFFFFu;
+        tv[i] = (i < per_thread) ? topk_idx[(int64_t)b * topk + min(e, topk - 1)] : -1;
     }
-    // exclusive scan of cnt over the workgroup (list order preserved)
-    int incl = cnt;
+    bool ok[4];
+    int32_t pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = e_begin + tid * per_thread + i;
+        const int64_t t = tv[i];
+        ok[i] = i < per_thread && e < e_end && t >= 0 && t < L && (t >> 6) < max_pages;
+        pv[i] = page_table[(int64_t)b * max_pages + (ok[i] ? (t >> 6) : 0)];
+    }
+    uint32_t rid[4];
+    int cnt_valid = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t page = pv[i];
+        rid[i] = (ok[i] && page >= 0 && page < num_pages)
+                     ? (uint32_t)(page * kPageRows + (tv[i] & 63))
+                     : 0xFFFFFFFFu;
+        cnt_valid += rid[i] != 0xFFFFFFFFu;
+    }
+    // exclusive scan of the counts over the workgroup (list order preserved)
+    int incl = cnt_valid;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
         const int v = __shfl_up(incl, d, 64);
         if (lane >= d) incl += v;
     }
     if (lane == 63) scan_lds[wave] = incl;
+    if (MB == 1) {  // rows 16..31 of both weight tiles stay zero: MFMA 32x32 over 16 heads
+        for (int i = tid; i < 16 * kPStride; i += kThreads) {
+            p_lds[0][16 * kPStride + i] = (_Float16)0.0f;
+            p_lds[1][16 * kPStride + i] = (_Float16)0.0f;
+        }
+    }
     __syncthreads();
-    int before = 0, n_valid = 0;
+    int before = 0, n_sum = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < 8; ++w) {
         const int s = scan_lds[w];
         before += (w < wave) ? s : 0;
-        n_valid += s;
+        n_sum += s;
     }
-    int pos = before + incl - cnt;
+    const int n_valid = __builtin_amdgcn_readfirstlane(n_sum);
+    int pos = before + incl - cnt_valid;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
         if (rid[i] != 0xFFFFFFFFu) rowid_lds[pos++] = rid[i];
-
-    // ---- query for this head group, resident in registers as f16 A operands ----
-    // A[m = head][k = 8g + i] at score step j holds dim 128g + 8j + i (latent,
-    // j < 16) or 512 + 16g + 8(j-16) + i (rope): the same permutation of the
-    // 576 dims that the unpacked rows use below.
-    half8_t qa[kKSteps];
-    {
-        const int head = hg * kHeads + n;
-        const uint16_t *qrow = q + ((int64_t)b * heads + head) * kDim;
-#pragma unroll
-        for (int j = 0; j < kKSteps; ++j) {
-            const int d0 = (j < 16) ? (128 * g + 8 * j) : (512 + 16 * g + 8 * (j - 16));
-            const uint4 v = *reinterpret_cast<const uint4 *>(qrow + d0);
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                qa[j][2 * i] = bf16_to_f16(w4[i] & 0xFFFFu);
-                qa[j][2 * i + 1] = bf16_to_f16(w4[i] >> 16);
-            }
-        }
-    }
-    __syncthreads();  // rowid_lds complete
-
-    const int n_tiles = (n_valid + kTile - 1) / kTile;
-    const int row = wave * 16 + n;  // this lane's row within a tile
-
-    float4_t o[8];
-    float m_run[4], l_run[4];
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) o[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.f; }
-
-    RowPart cur, nxt;
-    if (n_tiles > 0) load_part(cur, cache, rowid_lds[min(row, n_valid - 1)], row < n_valid, g);
-
-    for (int tile = 0; tile < n_tiles; ++tile) {
-        // (1) next tile's rows in flight while this one is processed
-        const int nrow = (tile + 1) * kTile + row;
-        if (tile + 1 < n_tiles)
-            load_part(nxt, cache, rowid_lds[min(nrow, n_valid - 1)], nrow < n_valid, g);
-        // every wave has finished reading the previous tile's values
-        if (tile > 0) __syncthreads();
-
-        // (2) unpack this wave's 16 rows, score them, store the latent part
-        half2_t s2[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const uint32_t byte = ((k < 4 ? cur.sc.x : cur.sc.y) >> (8 * (k & 3))) & 0xFFu;
-            s2[k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(byte * 0x0101u, 1.0f, false);
-        }
-        float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const uint4 nq = cur.nib[j >> 2];
-            const uint32_t d = (j & 3) == 0 ? nq.x : (j & 3) == 1 ? nq.y : (j & 3) == 2 ? nq.z : nq.w;
-            const half2_t sv = s2[j >> 1];
-            const half2_t e0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * sv;
-            const half2_t e1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * sv;
-            const half2_t e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * sv;
-            const half2_t e3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * sv;
-            const half8_t kb = join(e0, e1, e2, e3);
-            *reinterpret_cast<half8_t *>(v_lds + v_index(row, 128 * g + 8 * j)) = kb;
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j], kb, acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 16; j < 18; ++j) {
-            const uint32_t d0 = (j == 16) ? cur.rope.x : cur.rope.z;
-            const uint32_t d1 = (j == 16) ? cur.rope.y : cur.rope.w;
-            const half8_t kb = join(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false),
-                                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true),
-                                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false),
-                                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j], kb, acc, 0, 0, 0);
-        }
-
-        // (3) scores in log2 units; does any head's running max move?  It
-        // moves only when a score passes it by more than kSlack (weights stay
-        // <= 2^kSlack, fine in f16), so after the first tiles the max, the
-        // rescale and their cross-lane reductions are skipped.  The decision
-        // is shared by all waves.
-        const bool valid = tile * kTile + row < n_valid;
-        float x[4];
-        bool over = false;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            x[r] = valid ? acc[r] * scale_log2 : -INFINITY;
-            over |= x[r] > m_run[r] + kSlack;
-        }
-        const uint64_t ballot = __ballot(over);
-        if (lane == 0) flag_lds[wave] = ballot != 0;
-        __syncthreads();
-        if ((flag_lds[0] | flag_lds[1] | flag_lds[2] | flag_lds[3]) != 0) {
-            // exact tile maxima per head, exchanged through LDS
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float mx = row16_max(x[r]);
-                if (n == 0) wmax_lds[wave][4 * g + r] = mx;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int h = 4 * g + r;
-                const float mt = fmaxf(fmaxf(wmax_lds[0][h], wmax_lds[1][h]),
-                                       fmaxf(wmax_lds[2][h], wmax_lds[3][h]));
-                const float m_new = fmaxf(m_run[r], mt);
-                // m_new = -inf only while nothing valid was seen: keep zeros
-                const float alpha =
-                    (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[r] - m_new);
-                m_run[r] = m_new;
-                l_run[r] *= alpha;
-#pragma unroll
-                for (int nb = 0; nb < 8; ++nb) o[nb][r] *= alpha;
-            }
-        }
-
-        // (4) f16 weights to LDS; each lane keeps its own share of the sum
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float p =
-                (m_run[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[r] - m_run[r]);
-            const _Float16 ph = (_Float16)p;
-            p_lds[(4 * g + r) * kPStride + row] = ph;
-            l_run[r] += (float)ph;  // the normaliser sums the weights actually used
-        }
-        __syncthreads();
-
-        // (5) value contraction: this wave's 128 output columns, all 64 rows
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const half8_t pa = *reinterpret_cast<const half8_t *>(p_lds + n * kPStride + 32 * ks + 8 * g);
-            const int vr = 32 * ks + 8 * g + (n >> 2);
-            fp16x4_t vlo[8], vhi[8];
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                const int col = 128 * wave + 16 * nb + 4 * (n & 3);
-                vlo[nb] = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)(
-                    (__attribute__((address_space(3))) _Float16 *)(v_lds + v_index(vr, col))));
-                vhi[nb] = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)(
-                    (__attribute__((address_space(3))) _Float16 *)(v_lds + v_index(vr + 4, col))));
-            }
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                half8_t vb;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) { vb[i] = (_Float16)vlo[nb][i]; vb[4 + i] = (_Float16)vhi[nb][i]; }
-                o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[nb], 0, 0, 0);
-            }
-        }
-        cur = nxt;
-    }
-
-    // ---- epilogue: combine the lanes' and the waves' shares of the sums ----
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float ls = row16_sum(l_run[r]);
-        if (n == 0) lsum_lds[wave][4 * g + r] = ls;
-    }
     __syncthreads();
-    float l_tot[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int h = 4 * g + r;
-        l_tot[r] = lsum_lds[0][h] + lsum_lds[1][h] + lsum_lds[2][h] + lsum_lds[3][h];
-    }
+    // pad the last tile with copies of the last row: the loads then need no
+    // per-row guard, and the copies get zero weight
+    const int n_tiles = (n_valid + kTile - 1) / kTile;
+    const int n_pad = n_tiles * kTile;
+    if (n_valid > 0 && tid < n_pad - n_valid) rowid_lds[n_valid + tid] = rowid_lds[n_valid - 1];
+    __syncthreads();
 
-    if (splits == 1) {
-        const float ln2 = 0.69314718055994530942f;
+    // ---- tile ring: wave w issues the wave-wide loads i = w, w+8, w+16 of a
+    // tile; load i moves bytes [1024 i, 1024 i + 1024) of the 64 packed rows,
+    // lane l the 16-byte piece (64 i + l) % 22 of row (64 i + l) / 22.  Slot
+    // (tile % kNBuf); tile t is scored in step t and its values are
+    // contracted in step t + 1, so at step s the loads of tile s + kNBuf - 2
+    // go into the slot of tile s - 2 ----
+    const int n_dma = (wave + 16 < kDmaPerTile) ? 3 : 2;
+    int dma_row[3], dma_off[3];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int head = hg * kHeads + 4 * g + r;
-            const float inv = l_tot[r] > 0.f ? 1.0f / l_tot[r] : 0.f;
-            float *orow = out + ((int64_t)b * heads + head) * kLatent + 128 * wave + n;
+    for (int k = 0; k < 3; ++k) {
+        const int slot = 64 * (wave + 8 * k) + lane;
+        dma_row[k] = min(slot / 22, kTile - 1);
+        dma_off[k] = (slot % 22) * 16;
+    }
+    const uint32_t ring_addr = (uint32_t)(size_t)(lds_void_t *)ring;
+    auto issue = [&](int T) {
+        const uint32_t *rows = rowid_lds + T * kTile;
+        uint32_t r3[3];
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) orow[16 * nb] = o[nb][r] * inv;
-            if (wave == 0 && n == 0)
-                lse[(int64_t)b * heads + head] =
-                    l_tot[r] > 0.f ? (m_run[r] + log2f(l_tot[r])) * ln2 : -INFINITY;
+        for (int k = 0; k < 3; ++k) r3[k] = rows[dma_row[k]];
+        const uint32_t dst = ring_addr + (uint32_t)((T % kNBuf) * kTileBytes + wave * 1024);
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            if (k < n_dma)
+                dma16(cache + (size_t)r3[k] * kRowBytes + dma_off[k], dst + (uint32_t)(k * 8 * 1024));
+    };
+    // tile s is in LDS once at most the loads of the (up to kNBuf - 3) tiles
+    // issued after it are outstanding
+    auto wait_tile = [&](int s) {
+        const int after = min(kNBuf - 3, n_tiles - 1 - s);
+        if (after == kNBuf - 3) {
+            if (n_dma == 3) wait_vmcnt_n<3 * (kNBuf - 3)>();
+            else wait_vmcnt_n<2 * (kNBuf - 3)>();
+        } else {
+            wait_vmcnt(after * n_dma);
         }
+    };
+    if (wave < 4) {
+        // =========================== score waves ===========================
+        // The query in registers as f16 A operands: A[m = head][k = 8g+i] at
+        // score step j holds dim 128g + 8j + i (latent, j < 16) or
+        // 512 + 16g + 8(j-16) + i (rope), the dims the row unpack produces.
+        half8_t qa[MB][kKSteps];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const uint16_t *qrow = q + ((int64_t)b * heads + hg * HG + mb * 16 + n) * kDim;
+#pragma unroll
+            for (int j = 0; j < kKSteps; ++j) {
+                const int d0 = (j < 16) ? (128 * g + 8 * j) : (512 + 16 * g + 8 * (j - 16));
+                const uint4 v = *reinterpret_cast<const uint4 *>(qrow + d0);
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    qa[mb][j][2 * i] = bf16_to_f16(w4[i] & 0xFFFFu);
+                    qa[mb][j][2 * i + 1] = bf16_to_f16(w4[i] >> 16);
+                }
+            }
+        }
+        // the first tiles after the query, so that the query arrives first
+        // (loads complete in order)
+        for (int T = 0; T <= kNBuf - 3 && T < n_tiles; ++T) issue(T);
+        const int row = sw * 16 + n;  // this lane's row within a tile
+        float m_run[MB][4], l_run[MB][4], x[MB][4];
+        _Float16 ph[MB][4];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                m_run[mb][r] = -INFINITY;
+                l_run[mb][r] = 0.f;
+                x[mb][r] = -INFINITY;
+                ph[mb][r] = (_Float16)0.0f;
+            }
+
+        for (int s = 0; s <= n_tiles; ++s) {
+            if (s < n_tiles) wait_tile(s);
+            __syncthreads();                                            // B(s)
+            if (s + kNBuf - 2 < n_tiles) issue(s + kNBuf - 2);
+            // this wave's packed bytes of tile s, read before anything else
+            // so that the reads overlap the bookkeeping of tile s - 1
+            const uint8_t *rp = ring + (s % kNBuf) * kTileBytes + row * kRowBytes;
+            uint4 nib[4];
+            uint2 sc;
+            uint4 rope;
+            if (s < n_tiles) {
+#pragma unroll
+                for (int jp = 0; jp < 4; ++jp)
+                    nib[jp] = *reinterpret_cast<const uint4 *>(rp + 16 * (4 * g + jp));
+                sc = *reinterpret_cast<const uint2 *>(rp + kScaleOff + 8 * g);
+                rope = *reinterpret_cast<const uint4 *>(rp + kRopeOff + 16 * g);
+            }
+            if (s >= 1) {
+                const int pb = (s - 1) & 1;
+                const uint32_t f0 = flag_lds[pb][0], f1 = flag_lds[pb][1], f2 = flag_lds[pb][2],
+                               f3 = flag_lds[pb][3];
+                if ((f0 | f1 | f2 | f3) != 0) {
+                    // tile s-1 moved the running max: new max from the
+                    // flagged waves' tile maxima (every unflagged score lies
+                    // within kSlack of the old max), rescale, weights again
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int h = mb * 16 + 4 * g + r;
+                            float mt = -INFINITY;
+                            if (f0) mt = fmaxf(mt, red_lds[pb][0][h]);
+                            if (f1) mt = fmaxf(mt, red_lds[pb][1][h]);
+                            if (f2) mt = fmaxf(mt, red_lds[pb][2][h]);
+                            if (f3) mt = fmaxf(mt, red_lds[pb][3][h]);
+                            const float m_new = fmaxf(m_run[mb][r], mt);
+                            // -inf only while nothing valid was seen: keep zeros
+                            const float alpha = (m_new == -INFINITY)
+                                                    ? 1.0f
+                                                    : __builtin_amdgcn_exp2f(m_run[mb][r] - m_new);
+                            m_run[mb][r] = m_new;
+                            l_run[mb][r] *= alpha;
+                            if (sw == 0 && n == 0) alpha_lds[pb][h] = alpha;
+                            ph[mb][r] = (m_new == -INFINITY)
+                                            ? (_Float16)0.0f
+                                            : (_Float16)__builtin_amdgcn_exp2f(x[mb][r] - m_new);
+                            p_lds[pb][h * kPStride + row] = ph[mb][r];
+                        }
+                    __syncthreads();                                    // S(s)
+                }
+                // the normaliser sums the weights actually used
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) l_run[mb][r] += (float)ph[mb][r];
+            }
+            if (s == n_tiles) break;
+
+            // unpack this wave's 16 rows of tile s and score them
+            // {S,S} pairs for the 8 blocks 8g .. 8g+7 of this lane's dims
+            half2_t sp[8];
+            {
+                const uint32_t d0 = __builtin_amdgcn_perm(0u, sc.x, 0x01010000u);
+                const uint32_t d1 = __builtin_amdgcn_perm(0u, sc.x, 0x03030202u);
+                const uint32_t d2 = __builtin_amdgcn_perm(0u, sc.y, 0x01010000u);
+                const uint32_t d3 = __builtin_amdgcn_perm(0u, sc.y, 0x03030202u);
+                sp[0] = fp8x2<false>(d0); sp[1] = fp8x2<true>(d0);
+                sp[2] = fp8x2<false>(d1); sp[3] = fp8x2<true>(d1);
+                sp[4] = fp8x2<false>(d2); sp[5] = fp8x2<true>(d2);
+                sp[6] = fp8x2<false>(d3); sp[7] = fp8x2<true>(d3);
+            }
+            // two accumulators per head block (even / odd steps) keep 2 MB
+            // independent MFMA chains in flight
+            float4_t acc[MB][2];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                acc[mb][0] = float4_t{0.f, 0.f, 0.f, 0.f};
+                acc[mb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const uint32_t w = nib[j >> 2][j & 3];
+                const half2_t sv = sp[2 * (j >> 2) + ((j & 3) >> 1)];
+                const half8_t kb = join(fp4x2<0>(w) * sv, fp4x2<1>(w) * sv, fp4x2<2>(w) * sv,
+                                        fp4x2<3>(w) * sv);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[mb][j], kb, acc[mb][j & 1],
+                                                                           0, 0, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const half8_t kb = join(fp8x2<false>(rope[2 * t]), fp8x2<true>(rope[2 * t]),
+                                        fp8x2<false>(rope[2 * t + 1]), fp8x2<true>(rope[2 * t + 1]));
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[mb][16 + t], kb, acc[mb][t],
+                                                                       0, 0, 0);
+            }
+            // transposed f16 block scales of the tile for the value waves
+            const int pb = s & 1;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) st_lds[pb][(8 * g + k) * kSStride + row] = sp[k][0];
+
+            // softmax weights against the running max; a score that passes
+            // it by more than kSlack flags the tile (handled in step s + 1)
+            const bool full = (s + 1) * kTile <= n_valid;  // uniform: only the last tile is partial
+            const bool valid = full || s * kTile + row < n_valid;
+            bool over = false;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float sc_r = (acc[mb][0][r] + acc[mb][1][r]) * scale_log2;
+                    x[mb][r] = valid ? sc_r : -INFINITY;
+                    over |= x[mb][r] > m_run[mb][r] + kSlack;
+                    ph[mb][r] = (m_run[mb][r] == -INFINITY)
+                                    ? (_Float16)0.0f
+                                    : (_Float16)__builtin_amdgcn_exp2f(x[mb][r] - m_run[mb][r]);
+                    p_lds[pb][(mb * 16 + 4 * g + r) * kPStride + row] = ph[mb][r];
+                }
+            const bool flagged = __ballot(over) != 0;
+            if (lane == 0) flag_lds[pb][sw] = flagged;
+            if (flagged) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float mx = row16_max(x[mb][r]);
+                        if (n == 0) red_lds[pb][sw][mb * 16 + 4 * g + r] = mx;
+                    }
+            }
+        }
+        // sums over the lanes and waves, and the final max, for the value waves
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ls = row16_sum(l_run[mb][r]);
+                if (n == 0) sum_lds[sw][mb * 16 + 4 * g + r] = ls;
+                if (sw == 0 && n == 0) m_lds[mb * 16 + 4 * g + r] = m_run[mb][r];
+            }
+        __syncthreads();                                                // E
         return;
     }
 
-    // ---- split: publish the partial; the merge kernel combines them ----
-    // Partial layout per (unit, split): O[16][512] unnormalised, then m[16]
-    // (running max, log2 units) and l[16] (sum of weights).
-    const size_t pfl = (size_t)kHeads * kLatent + 2 * kHeads;
-    float *part = ws_partials + ((size_t)unit * splits + split) * pfl;
+    // =========================== value waves ===========================
+    // o[cb] (MFMA 32x32x16 C layout): head 8(i/4) + 4 g2 + i%4, column
+    // 128 sw + 32 cb + n32; step s contracts tile s - 1 with k = rows
+    // 32 rb + 16 g2 + 8 t + i at MFMA (rb, t)
+    for (int T = 0; T <= kNBuf - 3 && T < n_tiles; ++T) issue(T);
+    float16_t o[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int h = 4 * g + r;
-        float *prow = part + (size_t)h * kLatent + 128 * wave + n;
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) prow[16 * nb] = o[nb][r];
-        if (wave == 0 && n == 0) {
-            part[(size_t)kHeads * kLatent + h] = m_run[r];
-            part[(size_t)kHeads * kLatent + kHeads + h] = l_tot[r];
+        for (int i = 0; i < 16; ++i) o[cb][i] = 0.0f;
+
+    for (int s = 0; s <= n_tiles; ++s) {
+        if (s < n_tiles) wait_tile(s);
+        __syncthreads();                                                // B(s)
+        if (s + kNBuf - 2 < n_tiles) issue(s + kNBuf - 2);
+        if (s == 0) continue;
+        const int pb = (s - 1) & 1;
+        // every operand of tile s - 1, read before anything else: weights
+        // (A), packed values through the transposing 4-bit read (lanes
+        // 16G..16G+15 read 8 bytes = 16 columns of rows 32 rb + 16 (G/2) +
+        // 0..15; lane j of the group receives column j of those rows) and
+        // the rows' block scales
+        const uint8_t *tb = ring + ((s - 1) % kNBuf) * kTileBytes;
+        half8_t pa[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+            pa[rt] = *reinterpret_cast<const half8_t *>(p_lds[pb] + n32 * kPStride + 32 * (rt >> 1) +
+                                                        16 * g2 + 8 * (rt & 1));
+        int2_t vv[4][2];
+        half8_t sv[4][2][2];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int col0 = 128 * sw + 32 * cb;
+            const int blk = (col0 + n32) >> 4;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const int trow = 32 * rb + 16 * g2 + (lane & 15);
+                vv[cb][rb] = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_int2_t *)(
+                    (__attribute__((address_space(3))) uint8_t *)(tb + trow * kRowBytes +
+                                                                  (col0 >> 1) + 8 * ((lane >> 4) & 1))));
+                const half8_t *sp8 = reinterpret_cast<const half8_t *>(st_lds[pb] + blk * kSStride +
+                                                                       32 * rb + 16 * g2);
+                sv[cb][rb][0] = sp8[0];
+                sv[cb][rb][1] = sp8[1];
+            }
         }
+        if ((flag_lds[pb][0] | flag_lds[pb][1] | flag_lds[pb][2] | flag_lds[pb][3]) != 0) {
+            __syncthreads();                                            // S(s)
+            // the score waves rewrote the weights of tile s - 1 before S(s)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                pa[rt] = *reinterpret_cast<const half8_t *>(p_lds[pb] + n32 * kPStride +
+                                                            32 * (rt >> 1) + 16 * g2 + 8 * (rt & 1));
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int h = 8 * (i >> 2) + 4 * g2 + (i & 3);
+                    if (h < HG) o[cb][i] *= alpha_lds[pb][h];
+                }
+        }
+        // MFMA (rb, t) for every column block cb, so that four independent
+        // accumulator chains alternate
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int rb = rt >> 1, t = rt & 1;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const uint32_t w = (uint32_t)vv[cb][rb][t];
+                const half8_t ss = sv[cb][rb][t];
+                const half2_t s01 = {ss[0], ss[1]}, s23 = {ss[2], ss[3]}, s45 = {ss[4], ss[5]},
+                              s67 = {ss[6], ss[7]};
+                const half8_t vb = join(fp4x2<0>(w) * s01, fp4x2<1>(w) * s23, fp4x2<2>(w) * s45,
+                                        fp4x2<3>(w) * s67);
+                o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[rt], vb, o[cb], 0, 0, 0);
+            }
+        }
+    }
+    __syncthreads();                                                    // E
+
+    // ---- epilogue: normalise and store (or publish the split's partial) ----
+    const float ln2 = 0.69314718055994530942f;
+    const int vt = tid - 256;  // 0..255 over the value waves
+    if (splits == 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int h = 8 * (i >> 2) + 4 * g2 + (i & 3);
+            if (h >= HG) continue;
+            const float l_tot = sum_lds[0][h] + sum_lds[1][h] + sum_lds[2][h] + sum_lds[3][h];
+            const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+            float *orow = out + ((int64_t)b * heads + hg * HG + h) * kLatent + 128 * sw + n32;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) orow[32 * cb] = o[cb][i] * inv;
+        }
+        if (vt < HG) {
+            const float l_tot = sum_lds[0][vt] + sum_lds[1][vt] + sum_lds[2][vt] + sum_lds[3][vt];
+            lse[(int64_t)b * heads + hg * HG + vt] =
+                l_tot > 0.f ? (m_lds[vt] + log2f(l_tot)) * ln2 : -INFINITY;
+        }
+        return;
+    }
+    // split: the normalised partial (f16) and its (m, l) for the merge
+    // kernel.  Layout: part_o [unit][split][HG][512], part_ml
+    // [unit][split][HG][2] = (running max in log2 units, sum)
+    const size_t pidx = (size_t)unit * splits + split;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int h = 8 * (i >> 2) + 4 * g2 + (i & 3);
+        if (h >= HG) continue;
+        const float l_tot = sum_lds[0][h] + sum_lds[1][h] + sum_lds[2][h] + sum_lds[3][h];
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        _Float16 *prow = part_o + (pidx * HG + h) * kLatent + 128 * sw + n32;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) prow[32 * cb] = (_Float16)(o[cb][i] * inv);
+    }
+    if (vt < HG) {
+        const float l_tot = sum_lds[0][vt] + sum_lds[1][vt] + sum_lds[2][vt] + sum_lds[3][vt];
+        part_ml[(pidx * HG + vt) * 2] = m_lds[vt];
+        part_ml[(pidx * HG + vt) * 2 + 1] = l_tot;
     }
 }
 
-// Merge of the splits' partials: one thread per (unit, head, 4 columns); all
-// splits' loads are issued up front, then combined in split order (fixed,
-// hence deterministic):
-//   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,  O = sum_s 2^(m_s - M) O_s / L.
+// Merge of the splits' partials: one thread per (unit, head, 8 columns);
+// every split's loads are issued up front, then combined in split order
+// (fixed, hence deterministic):
+//   M = max_s m_s,  w_s = 2^(m_s - M) l_s,  out = sum_s w_s O_s / sum_s w_s,
+//   lse = ln 2 * (M + log2 sum_s w_s).
 __global__ __launch_bounds__(256) void merge_splits_kernel(
-    const float *__restrict__ ws_partials, float *__restrict__ out, float *__restrict__ lse,
-    int32_t heads, int32_t groups, int32_t splits, int32_t units) {
+    const _Float16 *__restrict__ part_o, const float *__restrict__ part_ml,
+    float *__restrict__ out, float *__restrict__ lse, int32_t heads, int32_t hg_size,
+    int32_t groups, int32_t splits, int32_t units) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)units * kHeads * (kLatent / 4);
+    const int64_t total = (int64_t)units * hg_size * (kLatent / 8);
     if (idx >= total) return;
-    const int c4 = (int)(idx % (kLatent / 4));
-    const int h = (int)((idx / (kLatent / 4)) % kHeads);
-    const int unit = (int)(idx / ((int64_t)(kLatent / 4) * kHeads));
-    const size_t pfl = (size_t)kHeads * kLatent + 2 * kHeads;
-    const float *base = ws_partials + (size_t)unit * splits * pfl;
+    const int c8 = (int)(idx % (kLatent / 8));
+    const int h = (int)((idx / (kLatent / 8)) % hg_size);
+    const int unit = (int)(idx / ((int64_t)(kLatent / 8) * hg_size));
     float ms[kMaxSplits], ls[kMaxSplits];
-    float4_t os[kMaxSplits];
+    half8_t os[kMaxSplits];
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s) {
         if (s < splits) {
-            const float *ps = base + s * pfl;
-            ms[s] = ps[(size_t)kHeads * kLatent + h];
-            ls[s] = ps[(size_t)kHeads * kLatent + kHeads + h];
-            os[s] = *reinterpret_cast<const float4_t *>(ps + (size_t)h * kLatent + 4 * c4);
+            const size_t pidx = ((size_t)unit * splits + s) * hg_size + h;
+            ms[s] = part_ml[pidx * 2];
+            ls[s] = part_ml[pidx * 2 + 1];
+            os[s] = *reinterpret_cast<const half8_t *>(part_o + pidx * kLatent + 8 * c8);
         } else {
             ms[s] = -INFINITY;
             ls[s] = 0.f;
-            os[s] = float4_t{0.f, 0.f, 0.f, 0.f};
+            os[s] = half8_t{};
         }
     }
     float M = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, ms[s]);
+    for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, ls[s] > 0.f ? ms[s] : -INFINITY);
     float L = 0.f;
-    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
 #pragma unroll
         for (int s = 0; s < kMaxSplits; ++s) {
-            const float w = __builtin_amdgcn_exp2f(ms[s] - M);
-            L += w * ls[s];
-            acc += w * os[s];
+            const float w = ls[s] > 0.f ? __builtin_amdgcn_exp2f(ms[s] - M) * ls[s] : 0.f;
+            L += w;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] += w * (float)os[s][k];
         }
     }
     const int b = unit / groups;
-    const int head = (unit % groups) * kHeads + h;
+    const int head = (unit % groups) * hg_size + h;
     const float inv = L > 0.f ? 1.0f / L : 0.f;
-    *reinterpret_cast<float4_t *>(out + ((int64_t)b * heads + head) * kLatent + 4 * c4) = acc * inv;
-    if (c4 == 0)
+    float4_t *orow = reinterpret_cast<float4_t *>(out + ((int64_t)b * heads + head) * kLatent + 8 * c8);
+    orow[0] = float4_t{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    orow[1] = float4_t{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+    if (c8 == 0)
         lse[(int64_t)b * heads + head] =
             L > 0.f ? (M + log2f(L)) * 0.69314718055994530942f : -INFINITY;
 }
@@ -451,10 +650,10 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(
 
 DecodePlan plan_decode(int batch, int heads, int topk) {
     DecodePlan p;
-    p.heads_per_group = kHeads;
-    p.groups = heads / kHeads;
+    p.heads_per_group = heads >= 32 ? 32 : 16;
+    p.groups = heads / p.heads_per_group;
     const int units = batch * p.groups;
-    const int target = 512;  // two workgroups per CU
+    const int target = 256;  // one workgroup per CU
     int s = (target + units - 1) / units;
     const int max_s = (topk + kTile - 1) / kTile;
     s = s < 1 ? 1 : s;
@@ -462,12 +661,14 @@ DecodePlan plan_decode(int batch, int heads, int topk) {
     s = s > kMaxSplits ? kMaxSplits : s;
     p.splits = s;
     p.per_split = (topk + s - 1) / s;
-    p.partial_floats = (size_t)kHeads * kLatent + 2 * kHeads;
+    p.partial_bytes = (size_t)p.heads_per_group * kLatent * sizeof(_Float16) +
+                      (size_t)p.heads_per_group * 2 * sizeof(float);
     if (s == 1) {
         p.workspace_bytes = 0;
     } else {
-        const size_t part = (size_t)units * s * p.partial_floats * sizeof(float);
-        p.workspace_bytes = (part + 255) & ~(size_t)255;
+        const size_t o_bytes = (size_t)units * s * p.heads_per_group * kLatent * sizeof(_Float16);
+        const size_t ml_bytes = (size_t)units * s * p.heads_per_group * 2 * sizeof(float);
+        p.workspace_bytes = ((o_bytes + 255) & ~(size_t)255) + ((ml_bytes + 255) & ~(size_t)255);
     }
     return p;
 }
@@ -479,18 +680,33 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
                                     float *out, float *lse, void *workspace,
                                     const DecodePlan &plan, hipStream_t stream) {
     const int blocks = ((batch + 7) / 8) * 8 * plan.groups * plan.splits;
-    float *partials = plan.splits > 1 ? static_cast<float *>(workspace) : nullptr;
+    const int units = batch * plan.groups;
+    _Float16 *part_o = nullptr;
+    float *part_ml = nullptr;
+    if (plan.splits > 1) {
+        const size_t o_bytes =
+            (size_t)units * plan.splits * plan.heads_per_group * kLatent * sizeof(_Float16);
+        part_o = static_cast<_Float16 *>(workspace);
+        part_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
+                                            ((o_bytes + 255) & ~(size_t)255));
+    }
     const float scale_log2 = (float)((double)scale * 1.4426950408889634074);
-    hipLaunchKernelGGL(sparse_mla_decode_kernel, dim3(blocks), dim3(kThreads), 0, stream, q, cache,
-                       num_pages, page_table, max_pages, seq_lens, topk_idx, heads, topk,
-                       scale_log2, out, lse, partials, batch, plan.groups, plan.splits,
-                       plan.per_split);
+    if (plan.heads_per_group == 32)
+        hipLaunchKernelGGL(sparse_mla_decode_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream,
+                           q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,
+                           topk, scale_log2, out, lse, part_o, part_ml, batch, plan.groups,
+                           plan.splits, plan.per_split);
+    else
+        hipLaunchKernelGGL(sparse_mla_decode_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream,
+                           q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,
+                           topk, scale_log2, out, lse, part_o, part_ml, batch, plan.groups,
+                           plan.splits, plan.per_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
-    const int units = batch * plan.groups;
-    const int64_t threads = (int64_t)units * kHeads * (kLatent / 4);
+    const int64_t threads = (int64_t)units * plan.heads_per_group * (kLatent / 8);
     hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       stream, partials, out, lse, heads, plan.groups, plan.splits, units);
+                       stream, part_o, part_ml, out, lse, heads, plan.heads_per_group,
+                       plan.groups, plan.splits, units);
     return hipGetLastError();
 }
 

@@ -38,10 +38,11 @@ def test_workspace_sizes():
     assert smla.decode_workspace_bytes(0, 64, 2048) == 0
     assert smla.decode_workspace_bytes(4, 32, 2048) == 0          # heads unsupported
     assert smla.decode_workspace_bytes(4, 64, 4096) == 0          # topk too large
-    # one sequence with 64 heads is split over many workgroups: partials of
-    # at least 16 heads x 512 columns each, for more than one split
+    # one sequence with 64 heads is split over many workgroups: f16 partials
+    # of at least 16 heads x 512 columns (+ fp32 max and sum) for each of
+    # more than one split
     ws = smla.decode_workspace_bytes(1, 64, 2048)
-    assert ws >= 2 * (16 * 512 + 32) * 4
+    assert ws >= 2 * (16 * 512 * 2 + 16 * 2 * 4)
     assert ws % 256 == 0
     assert smla.decode_workspace_bytes(64, 64, 2048) % 256 == 0
     # a single 64-entry list cannot be split
