@@ -10,28 +10,34 @@
 // query: "GLM-5.3 PCP/DCP long-context on H200", section 1.
 //
 // Work decomposition (gfx950: 256 CUs in 8 XCDs, 64-wide waves, 160 KB LDS):
-//   * one 256-thread workgroup (one wave per SIMD, up to 512 registers per
-//     lane) per (sequence, head group, split) and CU; a head group is 32
-//     heads (16 when a query has only 16), a split a slice of the top-k list;
-//   * prologue: the split's entries are validated, translated through the
-//     page table and compacted into LDS, so -1 padding and out-of-range
-//     entries cost neither a load nor a matrix instruction;
+//   * one 512-thread workgroup per (sequence, head group, split) and CU; a
+//     head group is 32 heads (16 when a query has only 16), a split a slice
+//     of the top-k list.  Waves 0-3 score, waves 4-7 contract values: one
+//     wave of each kind per SIMD, so the unpack work of one kind fills the
+//     VALU slots left by the other's matrix instructions;
+//   * prologue (value waves): the split's entries are validated, translated
+//     through the page table and compacted into LDS, so -1 padding and
+//     out-of-range entries cost neither a load nor a matrix instruction; the
+//     score waves load their query meanwhile;
 //   * the selected rows travel HBM -> LDS still packed (352 bytes each) by
-//     direct-to-LDS 16-byte loads: 64 rows = 22 wave-wide loads of
-//     consecutive bytes, four tiles in flight in a ring of five, so the
+//     direct-to-LDS 16-byte loads issued by the value waves: 64 rows = 22
+//     wave-wide loads of consecutive bytes; the three tiles after the one
+//     being scored are loaded or in flight, in a ring of five, so the
 //     gathers are coalesced and deep;
-//   * scores: each wave takes 16 rows of the tile; a lane reads the packed
-//     bytes of one row, unpacks them in registers (e2m1 -> f16 by the
+//   * scores: each score wave takes 16 rows of the tile; a lane reads the
+//     packed bytes of one row, unpacks them in registers (e2m1 -> f16 by the
 //     hardware converter, times the block scale with a packed f16 multiply,
 //     rope bytes E4M3 -> f16; all exact) and feeds MFMA 16x16x32 f16 against
 //     the query held in registers: one unpack serves every head of the group;
-//   * online softmax: the running max moves only when a score passes it by
-//     more than kSlack (log2 units), so normally no max reduction, rescale or
-//     extra barrier is needed;
-//   * values: each wave owns 128 of the 512 output columns; the transposing
-//     4-bit LDS read (ds_read_b64_tr_b4) hands a lane 16 rows of one column
-//     still packed, which are unpacked and scaled (scales from a per-tile
-//     transposed f16 table) and fed to MFMA 32x32x16 f16;
+//   * online softmax: the first tile sets the running max; after that it
+//     moves only when a score passes it by more than kSlack (log2 units), so
+//     normally no max reduction, rescale or extra barrier is needed; when it
+//     moves, the tile is re-weighted from its kept scores one step later;
+//   * values: each value wave owns 128 of the 512 output columns; the
+//     transposing 4-bit LDS read (ds_read_b64_tr_b4) hands a lane 16 rows of
+//     one column still packed, which are unpacked and scaled (scales from a
+//     per-tile transposed f16 table written by the score waves) and fed to
+//     MFMA 32x32x16 f16; the weight sums come from one more MFMA against ones;
 //   * all workgroups of one sequence run on the same XCD (consecutive
 //     workgroup ids go to consecutive XCDs), so head groups re-read shared
 //     rows from that XCD's L2;
@@ -46,6 +52,7 @@ namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef int int2_t __attribute__((ext_vector_type(2)));
@@ -54,13 +61,14 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kThreads = 512;                   // 4 score waves + 4 value waves, two per SIMD
 constexpr int kTile = 64;                       // selected rows per tile (16 per wave)
-constexpr int kNBuf = 5;                        // ring of packed tiles in LDS (3 in flight)
+constexpr int kNBuf = 5;                        // ring of packed tiles in LDS
 constexpr int kTileBytes = kTile * kRowBytes;   // 22,528
 constexpr int kDmaPerTile = kTileBytes / 1024;  // wave-wide 16-byte loads per tile (22)
 constexpr int kPStride = kTile + 8;             // f16 per softmax-weight row (144 B)
 constexpr int kSStride = kTile + 8;             // f16 per scale-table row (144 B)
 constexpr int kKSteps = kDim / 32;              // 18 score steps of 32
 constexpr float kSlack = 8.0f;                  // log2 headroom before the running max moves
+constexpr float kNoMax = -1.0e30f;              // running max before any valid score
 constexpr int kMaxSplits = 16;
 static_assert(kTileBytes % 1024 == 0, "a tile must be whole wave-wide loads");
 static_assert(kDmaPerTile > 16 && kDmaPerTile <= 24, "2 or 3 loads per wave per tile");
@@ -94,8 +102,10 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-__device__ __forceinline__ _Float16 bf16_to_f16(uint32_t h) {
-    return (_Float16)__uint_as_float(h << 16);
+// two BF16 values (low half first) -> two f16, rounded to nearest even
+__device__ __forceinline__ half2_t bf16x2_to_f16x2(uint32_t w) {
+    const float2_t f = {__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)};
+    return __builtin_convertvector(f, half2_t);
 }
 
 // e2m1 pair (byte SEL of w) -> f16 pair, exact
@@ -155,12 +165,12 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     __shared__ __attribute__((aligned(16))) _Float16 p_lds[2][32 * kPStride];
     __shared__ __attribute__((aligned(16))) _Float16 st_lds[2][32 * kSStride];
     __shared__ uint32_t rowid_lds[kMaxTopk];
-    __shared__ float red_lds[2][4][32];   // tile maxima of the score waves that flagged
+    __shared__ __attribute__((aligned(16))) float red_lds[2][4][32];  // per-wave tile maxima
     __shared__ float alpha_lds[2][32];    // rescale factors when the running max moved
     __shared__ float sum_lds[4][32];
     __shared__ float m_lds[32];
     __shared__ int32_t scan_lds[8];
-    __shared__ uint32_t flag_lds[2][4];
+    __shared__ __attribute__((aligned(16))) uint32_t flag_lds[2][4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -184,367 +194,485 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     const int e_begin = split * per_split;
     const int e_end = min(topk, e_begin + per_split);
 
-    // ---- prologue: validate, translate, compact the split's entries ----
-    // All index loads are issued before any is used (two round trips); an
-    // entry outside its range reads a harmless in-range word instead.
-    const int64_t L = seq_lens[b];
-    const int per_thread = (per_split + kThreads - 1) / kThreads;  // <= 4
-    int32_t tv[4];
+    // number of usable entries of the split, once the value waves have
+    // published their counts
+    auto count_valid = [&]() {
+        return __builtin_amdgcn_readfirstlane(scan_lds[0] + scan_lds[1] + scan_lds[2] + scan_lds[3]);
+    };
+    // ---- tile ring, loaded by the value waves: value wave v = w - 4 issues
+    // the wave-wide loads i = v, v+4, ..., v+20 of a tile; load i moves bytes
+    // [1024 i, 1024 i + 1024) of the 64 packed rows, lane l the 16-byte piece
+    // (64 i + l) % 22 of row (64 i + l) / 22.  Slot (tile % kNBuf); the
+    // value waves read tile t in step t + 1, so at step s the loads of tile
+    // s + kNBuf - 2 go into the slot of tile s - 2 ----
+    const int n_dma = (sw + 20 < kDmaPerTile) ? 6 : 5;
+    int dma_row[6], dma_off[6];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = e_begin + tid * per_thread + i;
-        tv[i] = (i < per_thread) ? topk_idx[(int64_t)b * topk + min(e, topk - 1)] : -1;
-    }
-    bool ok[4];
-    int32_t pv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = e_begin + tid * per_thread + i;
-        const int64_t t = tv[i];
-        ok[i] = i < per_thread && e < e_end && t >= 0 && t < L && (t >> 6) < max_pages;
-        pv[i] = page_table[(int64_t)b * max_pages + (ok[i] ? (t >> 6) : 0)];
-    }
-    uint32_t rid[4];
-    int cnt_valid = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t page = pv[i];
-        rid[i] = (ok[i] && page >= 0 && page < num_pages)
-                     ? (uint32_t)(page * kPageRows + (tv[i] & 63))
-                     : 0xFFFFFFFFu;
-        cnt_valid += rid[i] != 0xFFFFFFFFu;
-    }
-    // exclusive scan of the counts over the workgroup (list order preserved)
-    int incl = cnt_valid;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int v = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += v;
-    }
-    if (lane == 63) scan_lds[wave] = incl;
-    if (MB == 1) {  // rows 16..31 of both weight tiles stay zero: MFMA 32x32 over 16 heads
-        for (int i = tid; i < 16 * kPStride; i += kThreads) {
-            p_lds[0][16 * kPStride + i] = (_Float16)0.0f;
-            p_lds[1][16 * kPStride + i] = (_Float16)0.0f;
-        }
-    }
-    __syncthreads();
-    int before = 0, n_sum = 0;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-        const int s = scan_lds[w];
-        before += (w < wave) ? s : 0;
-        n_sum += s;
-    }
-    const int n_valid = __builtin_amdgcn_readfirstlane(n_sum);
-    int pos = before + incl - cnt_valid;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (rid[i] != 0xFFFFFFFFu) rowid_lds[pos++] = rid[i];
-    __syncthreads();
-    // pad the last tile with copies of the last row: the loads then need no
-    // per-row guard, and the copies get zero weight
-    const int n_tiles = (n_valid + kTile - 1) / kTile;
-    const int n_pad = n_tiles * kTile;
-    if (n_valid > 0 && tid < n_pad - n_valid) rowid_lds[n_valid + tid] = rowid_lds[n_valid - 1];
-    __syncthreads();
-
-    // ---- tile ring: wave w issues the wave-wide loads i = w, w+8, w+16 of a
-    // tile; load i moves bytes [1024 i, 1024 i + 1024) of the 64 packed rows,
-    // lane l the 16-byte piece (64 i + l) % 22 of row (64 i + l) / 22.  Slot
-    // (tile % kNBuf); tile t is scored in step t and its values are
-    // contracted in step t + 1, so at step s the loads of tile s + kNBuf - 2
-    // go into the slot of tile s - 2 ----
-    const int n_dma = (wave + 16 < kDmaPerTile) ? 3 : 2;
-    int dma_row[3], dma_off[3];
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        const int slot = 64 * (wave + 8 * k) + lane;
+    for (int k = 0; k < 6; ++k) {
+        const int slot = 64 * (sw + 4 * k) + lane;
         dma_row[k] = min(slot / 22, kTile - 1);
         dma_off[k] = (slot % 22) * 16;
     }
     const uint32_t ring_addr = (uint32_t)(size_t)(lds_void_t *)ring;
-    auto issue = [&](int T) {
+    // the row ids of this wave's loads of tile T, then the loads themselves
+    // (split so that the id reads can be issued early)
+    auto tile_rows = [&](int T, uint32_t (&r6)[6]) {
         const uint32_t *rows = rowid_lds + T * kTile;
-        uint32_t r3[3];
 #pragma unroll
-        for (int k = 0; k < 3; ++k) r3[k] = rows[dma_row[k]];
-        const uint32_t dst = ring_addr + (uint32_t)((T % kNBuf) * kTileBytes + wave * 1024);
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-            if (k < n_dma)
-                dma16(cache + (size_t)r3[k] * kRowBytes + dma_off[k], dst + (uint32_t)(k * 8 * 1024));
+        for (int k = 0; k < 6; ++k) r6[k] = rows[dma_row[k]];
     };
-    // tile s is in LDS once at most the loads of the (up to kNBuf - 3) tiles
-    // issued after it are outstanding
-    auto wait_tile = [&](int s) {
-        const int after = min(kNBuf - 3, n_tiles - 1 - s);
-        if (after == kNBuf - 3) {
-            if (n_dma == 3) wait_vmcnt_n<3 * (kNBuf - 3)>();
-            else wait_vmcnt_n<2 * (kNBuf - 3)>();
+    auto tile_dma = [&](int T, const uint32_t (&r6)[6]) {
+        const uint32_t dst = ring_addr + (uint32_t)((T % kNBuf) * kTileBytes + sw * 1024);
+#pragma unroll
+        for (int k = 0; k < 6; ++k)
+            if (k < n_dma)
+                dma16(cache + (size_t)r6[k] * kRowBytes + dma_off[k], dst + (uint32_t)(k * 4 * 1024));
+    };
+    auto issue = [&](int T) {
+        uint32_t r6[6];
+        tile_rows(T, r6);
+        tile_dma(T, r6);
+    };
+    // flags of the score waves for tile parity pb, as one 16-byte read
+    auto read_flags = [&](int pb) {
+        const uint4 f = *reinterpret_cast<const uint4 *>(&flag_lds[pb][0]);
+        return f;
+    };
+    // the flags as a wave-uniform bit mask (bit w: score wave w flagged)
+    auto flag_mask = [&](const uint4 &f) -> uint32_t {
+        return __builtin_amdgcn_readfirstlane((f.x ? 1u : 0u) | (f.y ? 2u : 0u) | (f.z ? 4u : 0u) |
+                                              (f.w ? 8u : 0u));
+    };
+    // tile t is in LDS once at most the loads of the tiles issued after it
+    // are outstanding: `after` of them (value waves only)
+    auto wait_tile = [&](int after) {
+        if (after == 1) {
+            if (n_dma == 6) wait_vmcnt_n<6>();
+            else wait_vmcnt_n<5>();
         } else {
             wait_vmcnt(after * n_dma);
         }
     };
     if (wave < 4) {
         // =========================== score waves ===========================
-        // The query in registers as f16 A operands: A[m = head][k = 8g+i] at
-        // score step j holds dim 128g + 8j + i (latent, j < 16) or
-        // 512 + 16g + 8(j-16) + i (rope), the dims the row unpack produces.
-        half8_t qa[MB][kKSteps];
+        // the query loads go out first, so that they overlap the value
+        // waves' index prologue; they are converted to f16 further down
+        uint4 qraw[MB][kKSteps];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const uint16_t *qrow = q + ((int64_t)b * heads + hg * HG + mb * 16 + n) * kDim;
 #pragma unroll
             for (int j = 0; j < kKSteps; ++j) {
                 const int d0 = (j < 16) ? (128 * g + 8 * j) : (512 + 16 * g + 8 * (j - 16));
-                const uint4 v = *reinterpret_cast<const uint4 *>(qrow + d0);
-                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    qa[mb][j][2 * i] = bf16_to_f16(w4[i] & 0xFFFFu);
-                    qa[mb][j][2 * i + 1] = bf16_to_f16(w4[i] >> 16);
-                }
+                qraw[mb][j] = *reinterpret_cast<const uint4 *>(qrow + d0);
             }
         }
-        // the first tiles after the query, so that the query arrives first
-        // (loads complete in order)
-        for (int T = 0; T <= kNBuf - 3 && T < n_tiles; ++T) issue(T);
-        const int row = sw * 16 + n;  // this lane's row within a tile
-        float m_run[MB][4], l_run[MB][4], x[MB][4];
-        _Float16 ph[MB][4];
+        if (MB == 1) {  // rows 16..31 of both weight tiles stay zero: MFMA 32x32 over 16 heads
+            for (int i = tid; i < 16 * kPStride; i += 256) {
+                p_lds[0][16 * kPStride + i] = (_Float16)0.0f;
+                p_lds[1][16 * kPStride + i] = (_Float16)0.0f;
+            }
+        }
+        // the two barriers of the value waves' prologue
+        __syncthreads();
+        const int n_valid = count_valid();
+        const int n_tiles = (n_valid + kTile - 1) / kTile;
+        __syncthreads();
+        // The query in registers as f16 A operands: A[m = head][k = 8g+i] at
+        // score step j holds dim 128g + 8j + i (latent, j < 16) or
+        // 512 + 16g + 8(j-16) + i (rope), the dims the row unpack produces.
+        half8_t qa[MB][kKSteps];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                m_run[mb][r] = -INFINITY;
-                l_run[mb][r] = 0.f;
-                x[mb][r] = -INFINITY;
-                ph[mb][r] = (_Float16)0.0f;
+            for (int j = 0; j < kKSteps; ++j) {
+                const uint32_t w4[4] = {qraw[mb][j].x, qraw[mb][j].y, qraw[mb][j].z, qraw[mb][j].w};
+                half2_t h[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) h[i] = bf16x2_to_f16x2(w4[i]);
+                qa[mb][j] = join(h[0], h[1], h[2], h[3]);
             }
+        // the value waves load the first tiles and wait until tile 0 is in LDS
+        __syncthreads();
+        const int row = sw * 16 + n;  // this lane's row within a tile
+        // running max per head (log2 units), set by the first tile
+        float m_run[MB][4];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) m_run[mb][r] = kNoMax;
 
-        for (int s = 0; s <= n_tiles; ++s) {
-            if (s < n_tiles) wait_tile(s);
-            __syncthreads();                                            // B(s)
-            if (s + kNBuf - 2 < n_tiles) issue(s + kNBuf - 2);
-            // this wave's packed bytes of tile s, read before anything else
-            // so that the reads overlap the bookkeeping of tile s - 1
-            const uint8_t *rp = ring + (s % kNBuf) * kTileBytes + row * kRowBytes;
+        // this wave's packed bytes of one tile: 4 x 16 B of nibbles (dims
+        // 128g .. 128g+127), the 8 block scales of those dims, 16 rope bytes
+        struct Packed {
             uint4 nib[4];
             uint2 sc;
             uint4 rope;
-            if (s < n_tiles) {
+        };
+        auto load_packed = [&](int T, Packed &pk) {
+            const uint8_t *rp = ring + (T % kNBuf) * kTileBytes + row * kRowBytes;
 #pragma unroll
-                for (int jp = 0; jp < 4; ++jp)
-                    nib[jp] = *reinterpret_cast<const uint4 *>(rp + 16 * (4 * g + jp));
-                sc = *reinterpret_cast<const uint2 *>(rp + kScaleOff + 8 * g);
-                rope = *reinterpret_cast<const uint4 *>(rp + kRopeOff + 16 * g);
-            }
-            if (s >= 1) {
-                const int pb = (s - 1) & 1;
-                const uint32_t f0 = flag_lds[pb][0], f1 = flag_lds[pb][1], f2 = flag_lds[pb][2],
-                               f3 = flag_lds[pb][3];
-                if ((f0 | f1 | f2 | f3) != 0) {
-                    // tile s-1 moved the running max: new max from the
-                    // flagged waves' tile maxima (every unflagged score lies
-                    // within kSlack of the old max), rescale, weights again
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int h = mb * 16 + 4 * g + r;
-                            float mt = -INFINITY;
-                            if (f0) mt = fmaxf(mt, red_lds[pb][0][h]);
-                            if (f1) mt = fmaxf(mt, red_lds[pb][1][h]);
-                            if (f2) mt = fmaxf(mt, red_lds[pb][2][h]);
-                            if (f3) mt = fmaxf(mt, red_lds[pb][3][h]);
-                            const float m_new = fmaxf(m_run[mb][r], mt);
-                            // -inf only while nothing valid was seen: keep zeros
-                            const float alpha = (m_new == -INFINITY)
-                                                    ? 1.0f
-                                                    : __builtin_amdgcn_exp2f(m_run[mb][r] - m_new);
-                            m_run[mb][r] = m_new;
-                            l_run[mb][r] *= alpha;
-                            if (sw == 0 && n == 0) alpha_lds[pb][h] = alpha;
-                            ph[mb][r] = (m_new == -INFINITY)
-                                            ? (_Float16)0.0f
-                                            : (_Float16)__builtin_amdgcn_exp2f(x[mb][r] - m_new);
-                            p_lds[pb][h * kPStride + row] = ph[mb][r];
-                        }
-                    __syncthreads();                                    // S(s)
-                }
-                // the normaliser sums the weights actually used
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) l_run[mb][r] += (float)ph[mb][r];
-            }
-            if (s == n_tiles) break;
-
-            // unpack this wave's 16 rows of tile s and score them
-            // {S,S} pairs for the 8 blocks 8g .. 8g+7 of this lane's dims
-            half2_t sp[8];
+            for (int jp = 0; jp < 4; ++jp)
+                pk.nib[jp] = *reinterpret_cast<const uint4 *>(rp + 16 * (4 * g + jp));
+            pk.sc = *reinterpret_cast<const uint2 *>(rp + kScaleOff + 8 * g);
+            pk.rope = *reinterpret_cast<const uint4 *>(rp + kRopeOff + 16 * g);
+        };
+        // unpack and score: x = scale_log2 * q.k of this wave's 16 rows (-inf
+        // for rows past the end of the list); sp = the {S,S} block-scale pairs
+        auto score = [&](int T, const Packed &pk, float (&x)[MB][4], half2_t (&sp)[8]) {
             {
-                const uint32_t d0 = __builtin_amdgcn_perm(0u, sc.x, 0x01010000u);
-                const uint32_t d1 = __builtin_amdgcn_perm(0u, sc.x, 0x03030202u);
-                const uint32_t d2 = __builtin_amdgcn_perm(0u, sc.y, 0x01010000u);
-                const uint32_t d3 = __builtin_amdgcn_perm(0u, sc.y, 0x03030202u);
+                const uint32_t d0 = __builtin_amdgcn_perm(0u, pk.sc.x, 0x01010000u);
+                const uint32_t d1 = __builtin_amdgcn_perm(0u, pk.sc.x, 0x03030202u);
+                const uint32_t d2 = __builtin_amdgcn_perm(0u, pk.sc.y, 0x01010000u);
+                const uint32_t d3 = __builtin_amdgcn_perm(0u, pk.sc.y, 0x03030202u);
                 sp[0] = fp8x2<false>(d0); sp[1] = fp8x2<true>(d0);
                 sp[2] = fp8x2<false>(d1); sp[3] = fp8x2<true>(d1);
                 sp[4] = fp8x2<false>(d2); sp[5] = fp8x2<true>(d2);
                 sp[6] = fp8x2<false>(d3); sp[7] = fp8x2<true>(d3);
             }
-            // two accumulators per head block (even / odd steps) keep 2 MB
-            // independent MFMA chains in flight
-            float4_t acc[MB][2];
+            float4_t acc[MB];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                acc[mb][0] = float4_t{0.f, 0.f, 0.f, 0.f};
-                acc[mb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
-            }
+            for (int mb = 0; mb < MB; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const uint32_t w = nib[j >> 2][j & 3];
+                const uint32_t w = pk.nib[j >> 2][j & 3];
                 const half2_t sv = sp[2 * (j >> 2) + ((j & 3) >> 1)];
                 const half8_t kb = join(fp4x2<0>(w) * sv, fp4x2<1>(w) * sv, fp4x2<2>(w) * sv,
                                         fp4x2<3>(w) * sv);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
-                    acc[mb][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[mb][j], kb, acc[mb][j & 1],
-                                                                           0, 0, 0);
+                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[mb][j], kb, acc[mb], 0, 0, 0);
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const half8_t kb = join(fp8x2<false>(rope[2 * t]), fp8x2<true>(rope[2 * t]),
-                                        fp8x2<false>(rope[2 * t + 1]), fp8x2<true>(rope[2 * t + 1]));
+                const half8_t kb = join(fp8x2<false>(pk.rope[2 * t]), fp8x2<true>(pk.rope[2 * t]),
+                                        fp8x2<false>(pk.rope[2 * t + 1]), fp8x2<true>(pk.rope[2 * t + 1]));
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
-                    acc[mb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[mb][16 + t], kb, acc[mb][t],
-                                                                       0, 0, 0);
+                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[mb][16 + t], kb, acc[mb], 0, 0, 0);
             }
-            // transposed f16 block scales of the tile for the value waves
-            const int pb = s & 1;
+            if ((T + 1) * kTile <= n_valid) {  // uniform: every tile but the last is full
 #pragma unroll
-            for (int k = 0; k < 8; ++k) st_lds[pb][(8 * g + k) * kSStride + row] = sp[k][0];
-
-            // softmax weights against the running max; a score that passes
-            // it by more than kSlack flags the tile (handled in step s + 1)
-            const bool full = (s + 1) * kTile <= n_valid;  // uniform: only the last tile is partial
-            const bool valid = full || s * kTile + row < n_valid;
-            bool over = false;
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) x[mb][r] = acc[mb][r] * scale_log2;
+            } else {
+                const bool valid = T * kTile + row < n_valid;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) x[mb][r] = valid ? acc[mb][r] * scale_log2 : -INFINITY;
+            }
+        };
+        // f16 softmax weights of a tile against the running max, to LDS
+        auto write_weights = [&](int pb, const float (&x)[MB][4]) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float sc_r = (acc[mb][0][r] + acc[mb][1][r]) * scale_log2;
-                    x[mb][r] = valid ? sc_r : -INFINITY;
-                    over |= x[mb][r] > m_run[mb][r] + kSlack;
-                    ph[mb][r] = (m_run[mb][r] == -INFINITY)
-                                    ? (_Float16)0.0f
-                                    : (_Float16)__builtin_amdgcn_exp2f(x[mb][r] - m_run[mb][r]);
-                    p_lds[pb][(mb * 16 + 4 * g + r) * kPStride + row] = ph[mb][r];
+                for (int r = 0; r < 4; ++r)
+                    p_lds[pb][(mb * 16 + 4 * g + r) * kPStride + row] =
+                        (_Float16)__builtin_amdgcn_exp2f(x[mb][r] - m_run[mb][r]);
+        };
+
+        Packed pk;
+        if (n_tiles > 0) load_packed(0, pk);
+        float xp[MB][4];  // scores of the previous tile, for a re-weight
+
+        for (int s = 0; s <= n_tiles + 1; ++s) {
+            __syncthreads();                                            // B(s)
+            // the flags of tile s - 1 (written in step s - 1), read early so
+            // that the read completes under the scoring
+            uint4 fl = {0u, 0u, 0u, 0u};
+            if (s >= 1 && s - 1 < n_tiles) fl = read_flags((s - 1) & 1);
+            // (a) scores of tile s from the bytes read during step s - 1
+            float x[MB][4];
+            half2_t sp[8];
+            if (s < n_tiles) score(s, pk, x, sp);
+            if (s == 0) {
+                // the first tile sets the running max: each wave's tile
+                // maxima through LDS (the parity-1 slots, which step 0 does
+                // not otherwise touch), one extra barrier F0 (the value
+                // waves are idle in step 0)
+                if (n_tiles > 0) {
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float mx = row16_max(x[mb][r]);
+                            if (n == 0) red_lds[1][sw][mb * 16 + 4 * g + r] = mx;
+                        }
                 }
-            const bool flagged = __ballot(over) != 0;
-            if (lane == 0) flag_lds[pb][sw] = flagged;
-            if (flagged) {
+                __syncthreads();                                        // F0
+                if (n_tiles > 0) {
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int h = mb * 16 + 4 * g + r;
+                            m_run[mb][r] = fmaxf(fmaxf(red_lds[1][0][h], red_lds[1][1][h]),
+                                                 fmaxf(red_lds[1][2][h], red_lds[1][3][h]));
+                        }
+                }
+            }
+            // (b) did tile s - 1 move the running max?  Then: new max from
+            // the waves' tile maxima (an unflagged wave published -inf, and
+            // its scores lie within kSlack of the old max), and tile s - 1
+            // is re-weighted from its kept scores before S(s); the value
+            // waves rescale O and the sum after S(s)
+            if (s >= 1 && s - 1 < n_tiles && flag_mask(fl) != 0) {
+                const int pb = (s - 1) & 1;
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float mx = row16_max(x[mb][r]);
-                        if (n == 0) red_lds[pb][sw][mb * 16 + 4 * g + r] = mx;
+                        const int h = mb * 16 + 4 * g + r;
+                        const float mt = fmaxf(fmaxf(m_run[mb][r], fmaxf(red_lds[pb][0][h], red_lds[pb][1][h])),
+                                               fmaxf(red_lds[pb][2][h], red_lds[pb][3][h]));
+                        if (sw == 0 && n == 0)
+                            alpha_lds[pb][h] = __builtin_amdgcn_exp2f(m_run[mb][r] - mt);
+                        m_run[mb][r] = mt;
                     }
+                write_weights(pb, xp);
+                __syncthreads();                                        // S(s)
             }
+            if (s >= n_tiles) continue;
+            // (c) this wave's packed bytes of tile s + 1 (complete since
+            // B(s)), issued first so that the reads complete under (d)
+            if (s + 1 < n_tiles) load_packed(s + 1, pk);
+            // (d) weights of tile s, the tile's transposed block scales for
+            // the value waves, and the flag (any score past max + kSlack)
+            const int pb = s & 1;
+            write_weights(pb, x);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) st_lds[pb][(8 * g + k) * kSStride + row] = sp[k][0];
+            bool over = false;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) over |= x[mb][r] > m_run[mb][r] + kSlack;
+            const bool flagged = __ballot(over) != 0;
+            if (lane == 0) flag_lds[pb][sw] = flagged;
+            // this wave's tile maxima per head (-inf when it did not flag)
+            float mx[MB][4];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mx[mb][r] = -INFINITY;
+            if (flagged) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mx[mb][r] = row16_max(x[mb][r]);
+            }
+            if (n == 0) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    *reinterpret_cast<float4_t *>(&red_lds[pb][sw][mb * 16 + 4 * g]) =
+                        float4_t{mx[mb][0], mx[mb][1], mx[mb][2], mx[mb][3]};
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) xp[mb][r] = x[mb][r];
         }
-        // sums over the lanes and waves, and the final max, for the value waves
+        // the final running max, for the value waves
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float ls = row16_sum(l_run[mb][r]);
-                if (n == 0) sum_lds[sw][mb * 16 + 4 * g + r] = ls;
+            for (int r = 0; r < 4; ++r)
                 if (sw == 0 && n == 0) m_lds[mb * 16 + 4 * g + r] = m_run[mb][r];
-            }
         __syncthreads();                                                // E
         return;
     }
 
+    // ---- prologue (value waves): validate, translate and compact the
+    // split's entries.  All index loads are issued before any is used (two
+    // round trips); an entry outside its range reads a harmless in-range word
+    // instead.  Thread v = tid - 256 takes entries [v per_thread, (v+1) per_thread) ----
+    const int per_thread = (per_split + 255) / 256;  // <= 8
+    uint32_t rid[8];
+    int cnt_valid = 0, incl = 0;
+    {
+        const int vt = tid - 256;
+        const int64_t L = seq_lens[b];
+        int32_t tv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = e_begin + vt * per_thread + i;
+            tv[i] = (i < per_thread) ? topk_idx[(int64_t)b * topk + min(e, topk - 1)] : -1;
+        }
+        bool ok[8];
+        int32_t pv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = e_begin + vt * per_thread + i;
+            const int64_t t = tv[i];
+            ok[i] = i < per_thread && e < e_end && t >= 0 && t < L && (t >> 6) < max_pages;
+            pv[i] = page_table[(int64_t)b * max_pages + (ok[i] ? (t >> 6) : 0)];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t page = pv[i];
+            rid[i] = (ok[i] && page >= 0 && page < num_pages)
+                         ? (uint32_t)(page * kPageRows + (tv[i] & 63))
+                         : 0xFFFFFFFFu;
+            cnt_valid += rid[i] != 0xFFFFFFFFu;
+        }
+        // inclusive scan of the counts within the wave (list order preserved)
+        incl = cnt_valid;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += v;
+        }
+        if (lane == 63) scan_lds[wave - 4] = incl;
+    }
+    __syncthreads();
+    const int n_valid = count_valid();
+    const int n_tiles = (n_valid + kTile - 1) / kTile;
+    // the last tile is padded with row 0 of page 0 (always in the cache): the
+    // loads then need no per-row guard, and the padding rows get zero weight
+    const int n_pad = n_tiles * kTile;
+    {
+        int pos = incl - cnt_valid;
+#pragma unroll
+        for (int w = 0; w < 3; ++w) pos += (w < wave - 4) ? scan_lds[w] : 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (rid[i] != 0xFFFFFFFFu) rowid_lds[pos++] = rid[i];
+        if (tid - 256 < n_pad - n_valid) rowid_lds[n_valid + tid - 256] = 0u;
+    }
+    __syncthreads();
+
     // =========================== value waves ===========================
     // o[cb] (MFMA 32x32x16 C layout): head 8(i/4) + 4 g2 + i%4, column
-    // 128 sw + 32 cb + n32; step s contracts tile s - 1 with k = rows
-    // 32 rb + 16 g2 + 8 t + i at MFMA (rb, t)
-    for (int T = 0; T <= kNBuf - 3 && T < n_tiles; ++T) issue(T);
-    float16_t o[4];
+    // 128 sw + 32 cb + n32; a tile's rows enter at MFMA (rb, t) as
+    // k = rows 32 rb + 16 g2 + 8 t + i
+    float16_t o[4], lacc;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int i = 0; i < 16; ++i) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[cb][i] = 0.0f;
+        for (int cb = 0; cb < 4; ++cb) o[cb][i] = 0.0f;
+        lacc[i] = 0.0f;
+    }
+    half8_t ones;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ones[i] = (_Float16)1.0f;
+    // operands of the tile awaiting contraction, held across one barrier:
+    // step s contracts tile s - 2 from registers (while the score waves
+    // score tile s), then reads the operands of tile s - 1
+    half8_t pa[4];
+    int2_t vv[4][2];
+    half8_t sv[4][2][2];
 
-    for (int s = 0; s <= n_tiles; ++s) {
-        if (s < n_tiles) wait_tile(s);
-        __syncthreads();                                                // B(s)
-        if (s + kNBuf - 2 < n_tiles) issue(s + kNBuf - 2);
-        if (s == 0) continue;
-        const int pb = (s - 1) & 1;
-        // every operand of tile s - 1, read before anything else: weights
-        // (A), packed values through the transposing 4-bit read (lanes
-        // 16G..16G+15 read 8 bytes = 16 columns of rows 32 rb + 16 (G/2) +
-        // 0..15; lane j of the group receives column j of those rows) and
-        // the rows' block scales
-        const uint8_t *tb = ring + ((s - 1) % kNBuf) * kTileBytes;
-        half8_t pa[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-            pa[rt] = *reinterpret_cast<const half8_t *>(p_lds[pb] + n32 * kPStride + 32 * (rt >> 1) +
-                                                        16 * g2 + 8 * (rt & 1));
-        int2_t vv[4][2];
-        half8_t sv[4][2][2];
+    // operands of tile s - 1 (read during step s, see below): the packed
+    // values through the transposing 4-bit read (lanes 16G..16G+15 read 8
+    // bytes = 16 columns of rows 32 rb + 16 (G/2) + 0..15; lane j of the
+    // group receives column j of those rows) and the rows' block scales.
+    // Reading a slot that holds no tile (before the first and after the
+    // last) is harmless: those operands are never used.
+    auto read_values = [&](int s, int rb) {
+        const int pb = (s + 1) & 1;  // parity of tile s - 1
+        const uint8_t *tb = ring + ((s + kNBuf - 1) % kNBuf) * kTileBytes;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             const int col0 = 128 * sw + 32 * cb;
             const int blk = (col0 + n32) >> 4;
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const int trow = 32 * rb + 16 * g2 + (lane & 15);
-                vv[cb][rb] = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_int2_t *)(
-                    (__attribute__((address_space(3))) uint8_t *)(tb + trow * kRowBytes +
-                                                                  (col0 >> 1) + 8 * ((lane >> 4) & 1))));
-                const half8_t *sp8 = reinterpret_cast<const half8_t *>(st_lds[pb] + blk * kSStride +
-                                                                       32 * rb + 16 * g2);
-                sv[cb][rb][0] = sp8[0];
-                sv[cb][rb][1] = sp8[1];
-            }
+            const int trow = 32 * rb + 16 * g2 + (lane & 15);
+            vv[cb][rb] = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_int2_t *)(
+                (__attribute__((address_space(3))) uint8_t *)(tb + trow * kRowBytes + (col0 >> 1) +
+                                                              8 * ((lane >> 4) & 1))));
+            const half8_t *sp8 =
+                reinterpret_cast<const half8_t *>(st_lds[pb] + blk * kSStride + 32 * rb + 16 * g2);
+            sv[cb][rb][0] = sp8[0];
+            sv[cb][rb][1] = sp8[1];
         }
-        if ((flag_lds[pb][0] | flag_lds[pb][1] | flag_lds[pb][2] | flag_lds[pb][3]) != 0) {
-            __syncthreads();                                            // S(s)
-            // the score waves rewrote the weights of tile s - 1 before S(s)
+    };
+
+    // the first tiles of the ring, then wait until tile 0 is in LDS (tile
+    // t + 1 is always complete one barrier before the score waves read it:
+    // they read it at the end of step t)
+    for (int T = 0; T <= kNBuf - 3 && T < n_tiles; ++T) issue(T);
+    if (n_tiles > 0) wait_tile(min(kNBuf - 3, n_tiles - 1));
+    __syncthreads();
+
+    for (int s = 0; s <= n_tiles + 1; ++s) {
+        // tile s + 1 complete before B(s): at most the tiles issued after it
+        // (s + 2 .. min(s + kNBuf - 3, n_tiles - 1)) may be outstanding
+        if (s + 1 < n_tiles) wait_tile(min(kNBuf - 4, n_tiles - 2 - s));
+        __syncthreads();                                                // B(s)
+        // step s contracts tile s - 2 (operands in registers) and reads the
+        // operands of tile s - 1; the flags of tile s - 1 say whether the
+        // score waves re-weight it before S(s)
+        const bool cur = s >= 1 && s - 1 < n_tiles;
+        uint4 fl = {0u, 0u, 0u, 0u};
+        if (cur) fl = read_flags((s - 1) & 1);
+        const bool more = s + kNBuf - 2 < n_tiles;
+        uint32_t r6[6];
+        if (more) tile_rows(s + kNBuf - 2, r6);
+        if (s == 0) __syncthreads();                                    // F0
+        // the weights of tile s - 1 (A operands); read again after S(s)
+        // when the score waves re-weight that tile
+        const int pb = (s - 1) & 1;
+        auto read_weights = [&](int rt) {
+            pa[rt] = *reinterpret_cast<const half8_t *>(p_lds[pb] + n32 * kPStride + 32 * (rt >> 1) +
+                                                        16 * g2 + 8 * (rt & 1));
+        };
+        if (s >= 2) {
+            // MFMA (rb, t) for every column block cb, so that four
+            // independent accumulator chains alternate; one more MFMA
+            // against ones sums this wave's quarter (rt = sw) of the weights.
+            // The operands of tile s - 1 replace those of tile s - 2 as soon
+            // as these are used up.
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-                pa[rt] = *reinterpret_cast<const half8_t *>(p_lds[pb] + n32 * kPStride +
-                                                            32 * (rt >> 1) + 16 * g2 + 8 * (rt & 1));
+            for (int rt = 0; rt < 4; ++rt) {
+                const int rb = rt >> 1, t = rt & 1;
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int h = 8 * (i >> 2) + 4 * g2 + (i & 3);
-                    if (h < HG) o[cb][i] *= alpha_lds[pb][h];
+                for (int cb = 0; cb < 4; ++cb) {
+                    const uint32_t w = (uint32_t)vv[cb][rb][t];
+                    const half8_t ss = sv[cb][rb][t];
+                    const half2_t s01 = {ss[0], ss[1]}, s23 = {ss[2], ss[3]}, s45 = {ss[4], ss[5]},
+                                  s67 = {ss[6], ss[7]};
+                    const half8_t vb = join(fp4x2<0>(w) * s01, fp4x2<1>(w) * s23, fp4x2<2>(w) * s45,
+                                            fp4x2<3>(w) * s67);
+                    o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[rt], vb, o[cb], 0, 0, 0);
                 }
-        }
-        // MFMA (rb, t) for every column block cb, so that four independent
-        // accumulator chains alternate
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const int rb = rt >> 1, t = rt & 1;
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                const uint32_t w = (uint32_t)vv[cb][rb][t];
-                const half8_t ss = sv[cb][rb][t];
-                const half2_t s01 = {ss[0], ss[1]}, s23 = {ss[2], ss[3]}, s45 = {ss[4], ss[5]},
-                              s67 = {ss[6], ss[7]};
-                const half8_t vb = join(fp4x2<0>(w) * s01, fp4x2<1>(w) * s23, fp4x2<2>(w) * s45,
-                                        fp4x2<3>(w) * s67);
-                o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[rt], vb, o[cb], 0, 0, 0);
+                if (rt == sw) lacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[rt], ones, lacc, 0, 0, 0);
+                read_weights(rt);
+                if (t == 1) read_values(s, rb);
             }
+        } else {
+            read_values(s, 0);
+            read_values(s, 1);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) read_weights(rt);
+        }
+        if (more) tile_dma(s + kNBuf - 2, r6);
+        if (cur && flag_mask(fl) != 0) {
+            // tile s - 1 moved the running max: the score waves re-weight
+            // it before S(s); O and the sum (tiles up to s - 2) are rescaled
+            __syncthreads();                                            // S(s)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int h = 8 * (i >> 2) + 4 * g2 + (i & 3);
+                if (h < HG) {
+                    const float a = alpha_lds[pb][h];
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb) o[cb][i] *= a;
+                    lacc[i] *= a;
+                }
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) read_weights(rt);
+        }
+    }
+    // this wave's quarter of the weight sums (all 32 columns of lacc are
+    // equal; lanes 0 and 32 hold the heads of g2 = 0 and 1)
+    if (n32 == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int h = 8 * (i >> 2) + 4 * g2 + (i & 3);
+            if (h < HG) sum_lds[sw][h] = lacc[i];
         }
     }
     __syncthreads();                                                    // E

@@ -216,6 +216,90 @@ def test_decode_invariances(dev, smla):
     assert np.max(np.abs(l3 - base_l)) < 1e-3
 
 
+def _bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _ascending_lists(case, cache_o, qmul):
+    """q times qmul, and every list reordered by ascending score (max over
+    heads), so that later tiles keep passing the running max by a wide
+    margin.  Returns the new case and the score of each list entry [B,H,K]
+    in log2 units."""
+    q = _bf16_to_f32(case["q"]) * np.float32(qmul)
+    case = dict(case, q=wl.bf16_bits(torch.from_numpy(q).to(torch.bfloat16)))
+    qf = _bf16_to_f32(case["q"]).astype(np.float64)
+    vals = oracle.dequant_rows(cache_o.reshape(-1, 352))
+    tk = case["topk"].copy()
+    B, H, K = qf.shape[0], qf.shape[1], tk.shape[1]
+    scores = np.full((B, H, K), -np.inf)
+    for b in range(B):
+        idx = tk[b][tk[b] >= 0].astype(np.int64)
+        rows = case["pt"][b][idx // 64].astype(np.int64) * 64 + idx % 64
+        sc = qf[b] @ vals[rows].T * case["scale"] / np.log(2.0)
+        order = np.argsort(sc.max(axis=0), kind="stable")
+        tk[b, :idx.size] = idx[order]
+        tk[b, idx.size:] = -1
+        scores[b, :, :idx.size] = sc[:, order]
+    case["topk"] = tk
+    return case, scores
+
+
+def _max_moves(scores, splits, slack=8.0):
+    """Tiles of 64 (per split of the list) whose maximum passes the maximum
+    of the earlier tiles of the same split by more than the slack."""
+    B, H, K = scores.shape
+    per = -(-K // splits)
+    moves = 0
+    for b in range(B):
+        for sp in range(splits):
+            seg = scores[b, :, sp * per:(sp + 1) * per]
+            run = None
+            for t0 in range(0, seg.shape[1], 64):
+                tm = seg[:, t0:t0 + 64].max(axis=1)
+                if run is not None:
+                    moves += int(np.any(tm > run + slack))
+                    run = np.maximum(run, tm)
+                else:
+                    run = tm
+    return moves
+
+
+def _shared_pages_case(batch, heads, pages, topk, seed):
+    """batch sequences whose page tables are permutations of the same
+    `pages` physical pages (one shared context), each with its own query and
+    its own top-k list: many sequences at the cost of quantising few rows."""
+    rng = np.random.default_rng(seed)
+    x = torch.randn((pages * 64, 576), generator=torch.Generator().manual_seed(seed))
+    x[:, rng.choice(576, 8, replace=False)] *= 8
+    bits = wl.bf16_bits(x.to(torch.bfloat16))
+    pt = np.stack([rng.permutation(pages) for _ in range(batch)]).astype(np.int32)
+    L = pages * 64
+    tk = np.stack([rng.choice(L, topk, replace=False) for _ in range(batch)]).astype(np.int32)
+    q = wl.bf16_bits(torch.randn((batch, heads, 576),
+                                 generator=torch.Generator().manual_seed(seed + 1)).to(torch.bfloat16))
+    return dict(q=q, rows=[bits], pt=pt, num_pages=pages, lens=np.full(batch, L, dtype=np.int64),
+                topk=tk, scale=1.0 / np.sqrt(576.0))
+
+
+@pytest.mark.parametrize("batch,heads", [(128, 16), (64, 64)])
+def test_decode_running_max_moves(dev, smla, batch, heads):
+    note("decode ascending lists B=%d H=%d" % (batch, heads))
+    case = _shared_pages_case(batch, heads, 40, 2048, seed=40 + heads)
+    cache_o = oracle_cache(case)
+    case, scores = _ascending_lists(case, cache_o, 16.0)
+    units = batch * max(1, heads // 32)
+    splits = min(-(-256 // units), 2048 // 64, 16)
+    # the re-weight path runs, on average, at least once per workgroup
+    assert _max_moves(scores, splits) >= units * splits
+    cache_d = gpu_cache(case, dev, smla)
+    out, lse = gpu_decode(case, cache_d, dev, smla)
+    ref_o, ref_l = oracle_decode(case, cache_o)
+    e_out, e_lse = rel_l2(out, ref_o), lse_err(lse, ref_l)
+    note("  rel_l2 %.3e lse %.3e" % (e_out, e_lse))
+    assert np.isfinite(out).all()
+    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+
+
 # --------------------------------------------------------------------------
 # full-size workloads: all queries on the GPU, sampled sequences on the oracle
 # --------------------------------------------------------------------------
