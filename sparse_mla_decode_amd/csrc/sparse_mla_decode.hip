@@ -255,8 +255,18 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     };
     if (wave < 4) {
         // =========================== score waves ===========================
-        // the query loads go out first, so that they overlap the value
-        // waves' index prologue; they are converted to f16 further down
+        if (MB == 1) {  // rows 16..31 of both weight tiles stay zero: MFMA 32x32 over 16 heads
+            for (int i = tid; i < 16 * kPStride; i += 256) {
+                p_lds[0][16 * kPStride + i] = (_Float16)0.0f;
+                p_lds[1][16 * kPStride + i] = (_Float16)0.0f;
+            }
+        }
+        // the two barriers of the value waves' prologue
+        __syncthreads();
+        // the query loads go out once the value waves' index loads have
+        // returned (so that those are not queued behind them), and overlap
+        // the rest of the prologue and the first tile loads; they are
+        // converted to f16 further down
         uint4 qraw[MB][kKSteps];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -267,14 +277,6 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                 qraw[mb][j] = *reinterpret_cast<const uint4 *>(qrow + d0);
             }
         }
-        if (MB == 1) {  // rows 16..31 of both weight tiles stay zero: MFMA 32x32 over 16 heads
-            for (int i = tid; i < 16 * kPStride; i += 256) {
-                p_lds[0][16 * kPStride + i] = (_Float16)0.0f;
-                p_lds[1][16 * kPStride + i] = (_Float16)0.0f;
-            }
-        }
-        // the two barriers of the value waves' prologue
-        __syncthreads();
         const int n_valid = count_valid();
         const int n_tiles = (n_valid + kTile - 1) / kTile;
         __syncthreads();
@@ -589,17 +591,20 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         }
     };
 
-    // the first tiles of the ring, then wait until tile 0 is in LDS (tile
-    // t + 1 is always complete one barrier before the score waves read it:
-    // they read it at the end of step t)
-    for (int T = 0; T <= kNBuf - 3 && T < n_tiles; ++T) issue(T);
-    if (n_tiles > 0) wait_tile(min(kNBuf - 3, n_tiles - 1));
+    // tiles 0 and 1 first (tile 2 follows once tile 0 is in, so that tile 0
+    // and the query are not queued behind it), then wait until tile 0 is in
+    // LDS.
+    // Tile t + 1 is complete one barrier before the score waves read it at
+    // the end of step t: before F0 for t = 0, before B(t) after that
+    for (int T = 0; T <= 1 && T < n_tiles; ++T) issue(T);
+    if (n_tiles > 0) wait_tile(min(1, n_tiles - 1));
     __syncthreads();
+    if (2 < n_tiles) issue(2);
 
     for (int s = 0; s <= n_tiles + 1; ++s) {
         // tile s + 1 complete before B(s): at most the tiles issued after it
         // (s + 2 .. min(s + kNBuf - 3, n_tiles - 1)) may be outstanding
-        if (s + 1 < n_tiles) wait_tile(min(kNBuf - 4, n_tiles - 2 - s));
+        if (s >= 1 && s + 1 < n_tiles) wait_tile(min(kNBuf - 4, n_tiles - 2 - s));
         __syncthreads();                                                // B(s)
         // step s contracts tile s - 2 (operands in registers) and reads the
         // operands of tile s - 1; the flags of tile s - 1 say whether the
@@ -610,7 +615,11 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         const bool more = s + kNBuf - 2 < n_tiles;
         uint32_t r6[6];
         if (more) tile_rows(s + kNBuf - 2, r6);
-        if (s == 0) __syncthreads();                                    // F0
+        if (s == 0) {
+            // tile 1 (read by the score waves after F0) is complete before F0
+            if (1 < n_tiles) wait_tile(2 < n_tiles ? 1 : 0);
+            __syncthreads();                                            // F0
+        }
         // the weights of tile s - 1 (A operands); read again after S(s)
         // when the score waves re-weight that tile
         const int pb = (s - 1) & 1;
@@ -719,21 +728,21 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     }
 }
 
-// Merge of the splits' partials: one thread per (unit, head, 8 columns);
-// every split's loads are issued up front, then combined in split order
-// (fixed, hence deterministic):
+// Merge of the splits' partials: one wave per (unit, head), a lane per 8
+// columns; the (m, l) pairs are wave-uniform (scalar loads), every split's
+// loads are issued up front, then combined in split order (fixed, hence
+// deterministic):
 //   M = max_s m_s,  w_s = 2^(m_s - M) l_s,  out = sum_s w_s O_s / sum_s w_s,
 //   lse = ln 2 * (M + log2 sum_s w_s).
 __global__ __launch_bounds__(256) void merge_splits_kernel(
     const _Float16 *__restrict__ part_o, const float *__restrict__ part_ml,
     float *__restrict__ out, float *__restrict__ lse, int32_t heads, int32_t hg_size,
     int32_t groups, int32_t splits, int32_t units) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)units * hg_size * (kLatent / 8);
-    if (idx >= total) return;
-    const int c8 = (int)(idx % (kLatent / 8));
-    const int h = (int)((idx / (kLatent / 8)) % hg_size);
-    const int unit = (int)(idx / ((int64_t)(kLatent / 8) * hg_size));
+    const int pair = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
+    if (pair >= units * hg_size) return;
+    const int lane = threadIdx.x & 63;
+    const int h = pair % hg_size;
+    const int unit = pair / hg_size;
     float ms[kMaxSplits], ls[kMaxSplits];
     half8_t os[kMaxSplits];
 #pragma unroll
@@ -742,7 +751,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(
             const size_t pidx = ((size_t)unit * splits + s) * hg_size + h;
             ms[s] = part_ml[pidx * 2];
             ls[s] = part_ml[pidx * 2 + 1];
-            os[s] = *reinterpret_cast<const half8_t *>(part_o + pidx * kLatent + 8 * c8);
+            os[s] = *reinterpret_cast<const half8_t *>(part_o + pidx * kLatent + 8 * lane);
         } else {
             ms[s] = -INFINITY;
             ls[s] = 0.f;
@@ -766,10 +775,10 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(
     const int b = unit / groups;
     const int head = (unit % groups) * hg_size + h;
     const float inv = L > 0.f ? 1.0f / L : 0.f;
-    float4_t *orow = reinterpret_cast<float4_t *>(out + ((int64_t)b * heads + head) * kLatent + 8 * c8);
+    float4_t *orow = reinterpret_cast<float4_t *>(out + ((int64_t)b * heads + head) * kLatent + 8 * lane);
     orow[0] = float4_t{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
     orow[1] = float4_t{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
-    if (c8 == 0)
+    if (lane == 0)
         lse[(int64_t)b * heads + head] =
             L > 0.f ? (M + log2f(L)) * 0.69314718055994530942f : -INFINITY;
 }
@@ -831,8 +840,8 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
                            plan.splits, plan.per_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
-    const int64_t threads = (int64_t)units * plan.heads_per_group * (kLatent / 8);
-    hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+    const int64_t pairs = (int64_t)units * plan.heads_per_group;  // one wave each
+    hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0,
                        stream, part_o, part_ml, out, lse, heads, plan.heads_per_group,
                        plan.groups, plan.splits, units);
     return hipGetLastError();
