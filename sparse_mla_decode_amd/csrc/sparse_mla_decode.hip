@@ -72,6 +72,8 @@ constexpr float kNoMax = -1.0e30f;              // running max before any valid 
 constexpr int kMaxSplits = 16;
 static_assert(kTileBytes % 1024 == 0, "a tile must be whole wave-wide loads");
 static_assert(kDmaPerTile > 16 && kDmaPerTile <= 24, "2 or 3 loads per wave per tile");
+static_assert(kNBuf >= 5 && 2 * kKSteps * 1024 <= 2 * kTileBytes,
+              "the query of 32 heads is staged in ring slots 3 and 4");
 
 __device__ __forceinline__ half8_t join(half2_t a, half2_t b, half2_t c, half2_t d) {
     half8_t r;
@@ -261,24 +263,26 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                 p_lds[1][16 * kPStride + i] = (_Float16)0.0f;
             }
         }
-        // the two barriers of the value waves' prologue
-        __syncthreads();
-        // the query loads go out once the value waves' index loads have
-        // returned (so that those are not queued behind them), and overlap
-        // the rest of the prologue and the first tile loads; they are
-        // converted to f16 further down
-        uint4 qraw[MB][kKSteps];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const uint16_t *qrow = q + ((int64_t)b * heads + hg * HG + mb * 16 + n) * kDim;
-#pragma unroll
-            for (int j = 0; j < kKSteps; ++j) {
-                const int d0 = (j < 16) ? (128 * g + 8 * j) : (512 + 16 * g + 8 * (j - 16));
-                qraw[mb][j] = *reinterpret_cast<const uint4 *>(qrow + d0);
-            }
+        // The query goes HBM -> LDS once per workgroup, by direct-to-LDS
+        // loads issued right away (score wave w issues the loads i = w, w+4,
+        // ...): load i = 18 mb + j puts, for every lane, that lane's A
+        // operand of score step j (heads 16 mb ..) into 1 KB of LDS, so each
+        // score wave reads its operands back with one linear 16-byte read per
+        // step.  The staging area is ring slots 3 and 4, which take their
+        // first tiles only after the initial barrier.
+        const uint32_t q_lds = ring_addr + 3u * kTileBytes;
+        for (int i = sw; i < MB * kKSteps; i += 4) {
+            const int mb = i / kKSteps, j = i % kKSteps;
+            const int d0 = (j < 16) ? (128 * g + 8 * j) : (512 + 16 * g + 8 * (j - 16));
+            dma16(q + ((int64_t)b * heads + hg * HG + mb * 16 + n) * kDim + d0,
+                  q_lds + (uint32_t)i * 1024u);
         }
+        // the two barriers of the value waves' prologue; the query is in LDS
+        // after the second
+        __syncthreads();
         const int n_valid = count_valid();
         const int n_tiles = (n_valid + kTile - 1) / kTile;
+        wait_vmcnt_n<0>();
         __syncthreads();
         // The query in registers as f16 A operands: A[m = head][k = 8g+i] at
         // score step j holds dim 128g + 8j + i (latent, j < 16) or
@@ -288,7 +292,9 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int j = 0; j < kKSteps; ++j) {
-                const uint32_t w4[4] = {qraw[mb][j].x, qraw[mb][j].y, qraw[mb][j].z, qraw[mb][j].w};
+                const uint4 v = *reinterpret_cast<const uint4 *>(
+                    ring + 3 * kTileBytes + (mb * kKSteps + j) * 1024 + 16 * lane);
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
                 half2_t h[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) h[i] = bf16x2_to_f16x2(w4[i]);
