@@ -606,6 +606,8 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     if (n_tiles > 0) wait_tile(min(1, n_tiles - 1));
     __syncthreads();
     if (2 < n_tiles) issue(2);
+    uint32_t r6[6];  // row ids of the next tile to load
+    if (3 < n_tiles) tile_rows(3, r6);
 
     for (int s = 0; s <= n_tiles + 1; ++s) {
         // tile s + 1 complete before B(s): at most the tiles issued after it
@@ -618,14 +620,16 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         const bool cur = s >= 1 && s - 1 < n_tiles;
         uint4 fl = {0u, 0u, 0u, 0u};
         if (cur) fl = read_flags((s - 1) & 1);
-        const bool more = s + kNBuf - 2 < n_tiles;
-        uint32_t r6[6];
-        if (more) tile_rows(s + kNBuf - 2, r6);
         if (s == 0) {
             // tile 1 (read by the score waves after F0) is complete before F0
             if (1 < n_tiles) wait_tile(2 < n_tiles ? 1 : 0);
             __syncthreads();                                            // F0
         }
+        // tile s + 3 into the slot of tile s - 2 (read for the last time in
+        // step s - 1), as early as possible; its row ids were read in step
+        // s - 1
+        const bool more = s + kNBuf - 2 < n_tiles;
+        if (more) tile_dma(s + kNBuf - 2, r6);
         // the weights of tile s - 1 (A operands); read again after S(s)
         // when the score waves re-weight that tile
         const int pb = (s - 1) & 1;
@@ -662,7 +666,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) read_weights(rt);
         }
-        if (more) tile_dma(s + kNBuf - 2, r6);
+        if (s + kNBuf - 1 < n_tiles) tile_rows(s + kNBuf - 1, r6);
         if (cur && flag_mask(fl) != 0) {
             // tile s - 1 moved the running max: the score waves re-weight
             // it before S(s); O and the sum (tiles up to s - 2) are rescaled
