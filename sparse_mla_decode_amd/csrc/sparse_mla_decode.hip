@@ -68,7 +68,6 @@ constexpr int kPStride = kTile + 8;             // f16 per softmax-weight row (1
 constexpr int kSStride = kTile + 8;             // f16 per scale-table row (144 B)
 constexpr int kKSteps = kDim / 32;              // 18 score steps of 32
 constexpr float kSlack = 8.0f;                  // log2 headroom before the running max moves
-constexpr float kNoMax = -1.0e30f;              // running max before any valid score
 constexpr int kMaxSplits = 16;
 static_assert(kTileBytes % 1024 == 0, "a tile must be whole wave-wide loads");
 static_assert(kDmaPerTile > 16 && kDmaPerTile <= 24, "2 or 3 loads per wave per tile");
@@ -303,12 +302,13 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         // the value waves load the first tiles and wait until tile 0 is in LDS
         __syncthreads();
         const int row = sw * 16 + n;  // this lane's row within a tile
-        // running max per head (log2 units), set by the first tile
+        // running max per head (log2 units), set by the first tile (0 while
+        // that tile is scored, so that its d are the scores themselves)
         float m_run[MB][4];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) m_run[mb][r] = kNoMax;
+            for (int r = 0; r < 4; ++r) m_run[mb][r] = 0.0f;
 
         // this wave's packed bytes of one tile: 4 x 16 B of nibbles (dims
         // 128g .. 128g+127), the 8 block scales of those dims, 16 rope bytes
@@ -325,9 +325,10 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
             pk.sc = *reinterpret_cast<const uint2 *>(rp + kScaleOff + 8 * g);
             pk.rope = *reinterpret_cast<const uint4 *>(rp + kRopeOff + 16 * g);
         };
-        // unpack and score: x = scale_log2 * q.k of this wave's 16 rows (-inf
-        // for rows past the end of the list); sp = the {S,S} block-scale pairs
-        auto score = [&](int T, const Packed &pk, float (&x)[MB][4], half2_t (&sp)[8]) {
+        // unpack and score: d = scale_log2 * q.k - m_run of this wave's 16
+        // rows (-inf for rows past the end of the list); sp = the {S,S}
+        // block-scale pairs
+        auto score = [&](int T, const Packed &pk, float (&d)[MB][4], half2_t (&sp)[8]) {
             {
                 const uint32_t d0 = __builtin_amdgcn_perm(0u, pk.sc.x, 0x01010000u);
                 const uint32_t d1 = __builtin_amdgcn_perm(0u, pk.sc.x, 0x03030202u);
@@ -363,28 +364,29 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) x[mb][r] = acc[mb][r] * scale_log2;
+                    for (int r = 0; r < 4; ++r) d[mb][r] = fmaf(acc[mb][r], scale_log2, -m_run[mb][r]);
             } else {
                 const bool valid = T * kTile + row < n_valid;
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) x[mb][r] = valid ? acc[mb][r] * scale_log2 : -INFINITY;
+                    for (int r = 0; r < 4; ++r)
+                        d[mb][r] = valid ? fmaf(acc[mb][r], scale_log2, -m_run[mb][r]) : -INFINITY;
             }
         };
-        // f16 softmax weights of a tile against the running max, to LDS
-        auto write_weights = [&](int pb, const float (&x)[MB][4]) {
+        // f16 softmax weights 2^d of a tile (d relative to the running max), to LDS
+        auto write_weights = [&](int pb, const float (&d)[MB][4]) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     p_lds[pb][(mb * 16 + 4 * g + r) * kPStride + row] =
-                        (_Float16)__builtin_amdgcn_exp2f(x[mb][r] - m_run[mb][r]);
+                        (_Float16)__builtin_amdgcn_exp2f(d[mb][r]);
         };
 
         Packed pk;
         if (n_tiles > 0) load_packed(0, pk);
-        float xp[MB][4];  // scores of the previous tile, for a re-weight
+        float dp[MB][4];  // d of the previous tile, for a re-weight
 
         for (int s = 0; s <= n_tiles + 1; ++s) {
             __syncthreads();                                            // B(s)
@@ -392,10 +394,11 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
             // that the read completes under the scoring
             uint4 fl = {0u, 0u, 0u, 0u};
             if (s >= 1 && s - 1 < n_tiles) fl = read_flags((s - 1) & 1);
-            // (a) scores of tile s from the bytes read during step s - 1
-            float x[MB][4];
+            // (a) scores of tile s from the bytes read during step s - 1,
+            // relative to the running max
+            float d[MB][4];
             half2_t sp[8];
-            if (s < n_tiles) score(s, pk, x, sp);
+            if (s < n_tiles) score(s, pk, d, sp);
             if (s == 0) {
                 // the first tile sets the running max: each wave's tile
                 // maxima through LDS (the parity-1 slots, which step 0 does
@@ -406,7 +409,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const float mx = row16_max(x[mb][r]);
+                            const float mx = row16_max(d[mb][r]);
                             if (n == 0) red_lds[1][sw][mb * 16 + 4 * g + r] = mx;
                         }
                 }
@@ -419,16 +422,19 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                             const int h = mb * 16 + 4 * g + r;
                             m_run[mb][r] = fmaxf(fmaxf(red_lds[1][0][h], red_lds[1][1][h]),
                                                  fmaxf(red_lds[1][2][h], red_lds[1][3][h]));
+                            d[mb][r] -= m_run[mb][r];
                         }
                 }
             }
             // (b) did tile s - 1 move the running max?  Then: new max from
             // the waves' tile maxima (an unflagged wave published -inf, and
-            // its scores lie within kSlack of the old max), and tile s - 1
-            // is re-weighted from its kept scores before S(s); the value
-            // waves rescale O and the sum after S(s)
+            // its scores lie within kSlack of the old max); tile s - 1 is
+            // re-weighted from its kept d before S(s), and the d of tile s
+            // are moved to the new max; the value waves rescale O and the
+            // sum after S(s)
             if (s >= 1 && s - 1 < n_tiles && flag_mask(fl) != 0) {
                 const int pb = (s - 1) & 1;
+                float shift[MB][4];
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -436,11 +442,13 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                         const int h = mb * 16 + 4 * g + r;
                         const float mt = fmaxf(fmaxf(m_run[mb][r], fmaxf(red_lds[pb][0][h], red_lds[pb][1][h])),
                                                fmaxf(red_lds[pb][2][h], red_lds[pb][3][h]));
-                        if (sw == 0 && n == 0)
-                            alpha_lds[pb][h] = __builtin_amdgcn_exp2f(m_run[mb][r] - mt);
+                        shift[mb][r] = m_run[mb][r] - mt;  // <= 0
+                        if (sw == 0 && n == 0) alpha_lds[pb][h] = __builtin_amdgcn_exp2f(shift[mb][r]);
                         m_run[mb][r] = mt;
+                        dp[mb][r] += shift[mb][r];
+                        d[mb][r] += shift[mb][r];
                     }
-                write_weights(pb, xp);
+                write_weights(pb, dp);
                 __syncthreads();                                        // S(s)
             }
             if (s >= n_tiles) continue;
@@ -450,14 +458,14 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
             // (d) weights of tile s, the tile's transposed block scales for
             // the value waves, and the flag (any score past max + kSlack)
             const int pb = s & 1;
-            write_weights(pb, x);
+            write_weights(pb, d);
 #pragma unroll
             for (int k = 0; k < 8; ++k) st_lds[pb][(8 * g + k) * kSStride + row] = sp[k][0];
             bool over = false;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) over |= x[mb][r] > m_run[mb][r] + kSlack;
+                for (int r = 0; r < 4; ++r) over |= d[mb][r] > kSlack;
             const bool flagged = __ballot(over) != 0;
             if (lane == 0) flag_lds[pb][sw] = flagged;
             // this wave's tile maxima per head (-inf when it did not flag)
@@ -470,7 +478,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) mx[mb][r] = row16_max(x[mb][r]);
+                    for (int r = 0; r < 4; ++r) mx[mb][r] = row16_max(d[mb][r]) + m_run[mb][r];
             }
             if (n == 0) {
 #pragma unroll
@@ -481,7 +489,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) xp[mb][r] = x[mb][r];
+                for (int r = 0; r < 4; ++r) dp[mb][r] = d[mb][r];
         }
         // the final running max, for the value waves
 #pragma unroll
