@@ -747,20 +747,25 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 }
 
 // Merge of the splits' partials: one wave per (unit, head), a lane per 8
-// columns; the (m, l) pairs are wave-uniform (scalar loads), every split's
-// loads are issued up front, then combined in split order (fixed, hence
+// columns; the wave of a head of sequence b runs on XCD b % 8, where the
+// decode workgroups of b wrote the partials (so they are read from that L2).
+// The (m, l) pairs are wave-uniform (scalar loads), every split's loads are
+// issued up front, then combined in split order (fixed, hence
 // deterministic):
 //   M = max_s m_s,  w_s = 2^(m_s - M) l_s,  out = sum_s w_s O_s / sum_s w_s,
 //   lse = ln 2 * (M + log2 sum_s w_s).
 __global__ __launch_bounds__(256) void merge_splits_kernel(
     const _Float16 *__restrict__ part_o, const float *__restrict__ part_ml,
     float *__restrict__ out, float *__restrict__ lse, int32_t heads, int32_t hg_size,
-    int32_t groups, int32_t splits, int32_t units) {
-    const int pair = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
-    if (pair >= units * hg_size) return;
+    int32_t groups, int32_t splits, int32_t batch) {
+    const int xcd = blockIdx.x & 7;
+    const int p = __builtin_amdgcn_readfirstlane((int)(blockIdx.x >> 3) * 4 + (int)(threadIdx.x >> 6));
+    const int per_seq = groups * hg_size;
+    const int b = (p / per_seq) * 8 + xcd;
+    if (b >= batch) return;
     const int lane = threadIdx.x & 63;
-    const int h = pair % hg_size;
-    const int unit = pair / hg_size;
+    const int h = p % hg_size;
+    const int unit = b * groups + (p % per_seq) / hg_size;
     float ms[kMaxSplits], ls[kMaxSplits];
     half8_t os[kMaxSplits];
 #pragma unroll
@@ -790,7 +795,6 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(
             for (int k = 0; k < 8; ++k) acc[k] += w * (float)os[s][k];
         }
     }
-    const int b = unit / groups;
     const int head = (unit % groups) * hg_size + h;
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     float4_t *orow = reinterpret_cast<float4_t *>(out + ((int64_t)b * heads + head) * kLatent + 8 * lane);
@@ -858,10 +862,11 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
                            plan.splits, plan.per_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
-    const int64_t pairs = (int64_t)units * plan.heads_per_group;  // one wave each
-    hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0,
+    // one wave per (unit, head); the blocks of XCD x take the sequences b = x mod 8
+    const int64_t per_xcd = (int64_t)((batch + 7) / 8) * plan.groups * plan.heads_per_group;
+    hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)(8 * ((per_xcd + 3) / 4))), dim3(256), 0,
                        stream, part_o, part_ml, out, lse, heads, plan.heads_per_group,
-                       plan.groups, plan.splits, units);
+                       plan.groups, plan.splits, batch);
     return hipGetLastError();
 }
 
