@@ -587,19 +587,23 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     // group receives column j of those rows) and the rows' block scales.
     // Reading a slot that holds no tile (before the first and after the
     // last) is harmless: those operands are never used.
+    // lane parts of the LDS addresses (bytes): packed values (row
+    // 16 g2 + lane % 16 of the 32-row half, columns 128 sw + 16 (lane / 16 % 2)
+    // ..), block scales (block 8 sw + n32 / 16, rows 16 g2 ..), weights
+    // (head n32, rows 16 g2 ..); the rest of each address is a constant
+    const uint32_t v_lane = (uint32_t)((16 * g2 + (lane & 15)) * kRowBytes + 64 * sw + 8 * ((lane >> 4) & 1));
+    const uint32_t s_lane = (uint32_t)(((8 * sw + (n32 >> 4)) * kSStride + 16 * g2) * 2);
+    const uint32_t p_lane = (uint32_t)((n32 * kPStride + 16 * g2) * 2);
     auto read_values = [&](int s, int rb) {
         const int pb = (s + 1) & 1;  // parity of tile s - 1
-        const uint8_t *tb = ring + ((s + kNBuf - 1) % kNBuf) * kTileBytes;
+        const uint8_t *vb = ring + ((s + kNBuf - 1) % kNBuf) * kTileBytes + v_lane;
+        const uint8_t *sb = reinterpret_cast<const uint8_t *>(st_lds[pb]) + s_lane;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            const int col0 = 128 * sw + 32 * cb;
-            const int blk = (col0 + n32) >> 4;
-            const int trow = 32 * rb + 16 * g2 + (lane & 15);
+            // columns 128 sw + 32 cb + n32: packed bytes 16 cb further, block 2 cb further
             vv[cb][rb] = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_int2_t *)(
-                (__attribute__((address_space(3))) uint8_t *)(tb + trow * kRowBytes + (col0 >> 1) +
-                                                              8 * ((lane >> 4) & 1))));
-            const half8_t *sp8 =
-                reinterpret_cast<const half8_t *>(st_lds[pb] + blk * kSStride + 32 * rb + 16 * g2);
+                (__attribute__((address_space(3))) const uint8_t *)(vb + 32 * rb * kRowBytes + 16 * cb)));
+            const half8_t *sp8 = reinterpret_cast<const half8_t *>(sb + (2 * cb * kSStride + 32 * rb) * 2);
             sv[cb][rb][0] = sp8[0];
             sv[cb][rb][1] = sp8[1];
         }
@@ -622,6 +626,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         // (s + 2 .. min(s + kNBuf - 3, n_tiles - 1)) may be outstanding
         if (s >= 1 && s + 1 < n_tiles) wait_tile(min(kNBuf - 4, n_tiles - 2 - s));
         __syncthreads();                                                // B(s)
+        asm volatile("" : "+v"(ones));  // kept in registers, not rebuilt per use
         // step s contracts tile s - 2 (operands in registers) and reads the
         // operands of tile s - 1; the flags of tile s - 1 say whether the
         // score waves re-weight it before S(s)
@@ -641,9 +646,9 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         // the weights of tile s - 1 (A operands); read again after S(s)
         // when the score waves re-weight that tile
         const int pb = (s - 1) & 1;
+        const uint8_t *wb = reinterpret_cast<const uint8_t *>(p_lds[pb]) + p_lane;
         auto read_weights = [&](int rt) {
-            pa[rt] = *reinterpret_cast<const half8_t *>(p_lds[pb] + n32 * kPStride + 32 * (rt >> 1) +
-                                                        16 * g2 + 8 * (rt & 1));
+            pa[rt] = *reinterpret_cast<const half8_t *>(wb + (32 * (rt >> 1) + 8 * (rt & 1)) * 2);
         };
         if (s >= 2) {
             // MFMA (rb, t) for every column block cb, so that four
