@@ -27,6 +27,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 ROW_BYTES = 352
+FP8_ROW_BYTES = 576
 PAGE_ROWS = 64
 LATENT = 512
 DIM = 576
@@ -77,6 +78,15 @@ def _load():
     lib.oracle_sparse_mla_decode.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, dbl,
                                              P, P, ctypes.c_int]
     lib.oracle_sparse_mla_decode.restype = None
+    lib.oracle_quant_rows_fp8.argtypes = [P, i64, P]
+    lib.oracle_quant_rows_fp8.restype = None
+    lib.oracle_dequant_rows_fp8.argtypes = [P, i64, P]
+    lib.oracle_dequant_rows_fp8.restype = None
+    lib.oracle_kv_quant_append_fp8.argtypes = [P, i64, P, P, i64]
+    lib.oracle_kv_quant_append_fp8.restype = i64
+    lib.oracle_sparse_mla_decode_fp8.argtypes = lib.oracle_sparse_mla_decode.argtypes
+    lib.oracle_sparse_mla_decode_fp8.restype = None
+    lib.oracle_fp8_row_bytes.restype = ctypes.c_int
     lib.oracle_row_bytes.restype = ctypes.c_int
     lib.oracle_page_rows.restype = ctypes.c_int
     _lib = lib
@@ -159,22 +169,58 @@ def kv_quant_append(rows_bf16_bits: np.ndarray, slot_mapping: np.ndarray,
                                               cache.shape[0]))
 
 
+def quant_rows_fp8(rows_bf16_bits: np.ndarray) -> np.ndarray:
+    """[n,576] uint16 (BF16 bit patterns) -> [n,576] uint8 lean FP8 rows."""
+    x = _c(rows_bf16_bits, np.uint16)
+    assert x.ndim == 2 and x.shape[1] == DIM, x.shape
+    out = np.zeros((x.shape[0], FP8_ROW_BYTES), dtype=np.uint8)
+    if x.shape[0]:
+        _load().oracle_quant_rows_fp8(_ptr(x), x.shape[0], _ptr(out))
+    return out
+
+
+def dequant_rows_fp8(rows: np.ndarray) -> np.ndarray:
+    """[n,576] uint8 lean FP8 rows -> [n,576] float64 exact values."""
+    r = _c(rows, np.uint8)
+    assert r.ndim == 2 and r.shape[1] == FP8_ROW_BYTES, r.shape
+    out = np.zeros((r.shape[0], DIM), dtype=np.float64)
+    if r.shape[0]:
+        _load().oracle_dequant_rows_fp8(_ptr(r), r.shape[0], _ptr(out))
+    return out
+
+
+def kv_quant_append_fp8(rows_bf16_bits: np.ndarray, slot_mapping: np.ndarray,
+                        cache: np.ndarray) -> int:
+    """Quantise rows into the lean FP8 ``cache`` ([P,64,576] uint8, in place)."""
+    x = _c(rows_bf16_bits, np.uint16)
+    s = _c(slot_mapping, np.int32)
+    assert cache.dtype == np.uint8 and cache.flags.c_contiguous
+    assert cache.ndim == 3 and cache.shape[1:] == (PAGE_ROWS, FP8_ROW_BYTES)
+    assert x.shape == (s.shape[0], DIM)
+    return int(_load().oracle_kv_quant_append_fp8(_ptr(x), x.shape[0], _ptr(s), _ptr(cache),
+                                                  cache.shape[0]))
+
+
 def sparse_mla_decode(q_bf16_bits: np.ndarray, cache: np.ndarray, page_table: np.ndarray,
                       seq_lens: np.ndarray, topk: np.ndarray, softmax_scale: float,
                       nthreads: int = 0):
-    """Returns (out [B,H,512] float64, lse [B,H] float64)."""
+    """Returns (out [B,H,512] float64, lse [B,H] float64).  The cache's row
+    size selects the format: [P,64,352] NVFP4 rows or [P,64,576] lean FP8
+    rows."""
     q = _c(q_bf16_bits, np.uint16)
     c = _c(cache, np.uint8)
     pt = _c(page_table, np.int32)
     sl = _c(seq_lens, np.int32)
     tk = _c(topk, np.int32)
     B, H, D = q.shape
-    assert D == DIM and c.ndim == 3 and c.shape[1:] == (PAGE_ROWS, ROW_BYTES)
+    assert D == DIM and c.ndim == 3 and c.shape[1] == PAGE_ROWS
+    assert c.shape[2] in (ROW_BYTES, FP8_ROW_BYTES), c.shape
     assert pt.ndim == 2 and pt.shape[0] == B and sl.shape == (B,)
     assert tk.ndim == 2 and tk.shape[0] == B
     out = np.zeros((B, H, LATENT), dtype=np.float64)
     lse = np.zeros((B, H), dtype=np.float64)
-    _load().oracle_sparse_mla_decode(_ptr(q), _ptr(c), c.shape[0], _ptr(pt), pt.shape[1],
-                                     _ptr(sl), _ptr(tk), B, H, tk.shape[1],
-                                     float(softmax_scale), _ptr(out), _ptr(lse), int(nthreads))
+    lib = _load()
+    fn = lib.oracle_sparse_mla_decode if c.shape[2] == ROW_BYTES else lib.oracle_sparse_mla_decode_fp8
+    fn(_ptr(q), _ptr(c), c.shape[0], _ptr(pt), pt.shape[1], _ptr(sl), _ptr(tk), B, H, tk.shape[1],
+       float(softmax_scale), _ptr(out), _ptr(lse), int(nthreads))
     return out, lse

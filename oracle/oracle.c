@@ -39,7 +39,11 @@
  *     an empty selection gives out = 0 and lse = -inf;
  *   - an index t is used iff 0 <= t < L_b, t/64 < max_pages and its physical
  *     page lies in [0, num_pages); anything else (-1 padding included) is
- *     skipped; a repeated index counts once per occurrence.
+ *     skipped; a repeated index counts once per occurrence;
+ *   - the lean FP8 row the byte table of [P1] compares against is the 576
+ *     values as OCP E4M3 bytes in dim order (latent then rope), no scale,
+ *     each the E4M3 value nearest the input (ties to even, saturating at
+ *     448, sign copied) -- the same rule as the NVFP4 row's rope bytes.
  *
  * Inputs must be finite; behaviour on NaN/Inf inputs is not defined here.
  */
@@ -60,6 +64,7 @@
 #define SCALE_OFF NIB_BYTES
 #define ROPE_OFF (SCALE_OFF + NBLOCKS)
 #define ROW_BYTES (ROPE_OFF + ROPE)
+#define FP8_ROW_BYTES DIM
 #define PAGE_ROWS 64
 
 /* ---------------------------------------------------------------------- */
@@ -244,6 +249,53 @@ int64_t oracle_kv_quant_append(const uint16_t *x, int64_t n, const int32_t *slot
 }
 
 /* ---------------------------------------------------------------------- */
+/* Lean FP8 rows [P1 byte table: 576 B per row in FP8]                       */
+/* ---------------------------------------------------------------------- */
+
+/* One 576-value BF16 row -> 576 E4M3 bytes, dim order, no scale. */
+void oracle_quant_row_fp8(const uint16_t *x, uint8_t *row)
+{
+    for (int d = 0; d < DIM; ++d)
+        row[d] = oracle_e4m3_nearest(bf16_value(x[d]), 1.0);
+}
+
+/* One 576-byte FP8 row -> its 576 exact values. */
+void oracle_dequant_row_fp8(const uint8_t *row, double *k)
+{
+    for (int d = 0; d < DIM; ++d)
+        k[d] = oracle_e4m3_value(row[d]);
+}
+
+void oracle_quant_rows_fp8(const uint16_t *x, int64_t n, uint8_t *rows)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; ++i)
+        oracle_quant_row_fp8(x + i * DIM, rows + i * FP8_ROW_BYTES);
+}
+
+void oracle_dequant_rows_fp8(const uint8_t *rows, int64_t n, double *k)
+{
+    for (int64_t i = 0; i < n; ++i)
+        oracle_dequant_row_fp8(rows + i * FP8_ROW_BYTES, k + i * DIM);
+}
+
+/* Paged append of FP8 rows: the slot rules of oracle_kv_quant_append. */
+int64_t oracle_kv_quant_append_fp8(const uint16_t *x, int64_t n, const int32_t *slot_mapping,
+                                   uint8_t *cache, int64_t num_pages)
+{
+    int64_t written = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t s = slot_mapping[i];
+        if (s < 0 || s >= num_pages * PAGE_ROWS)
+            continue;
+        oracle_quant_row_fp8(x + i * DIM, cache + s * FP8_ROW_BYTES);
+        ++written;
+    }
+    return written;
+}
+
+/* ---------------------------------------------------------------------- */
 /* Sparse MLA decode                                                         */
 /* ---------------------------------------------------------------------- */
 
@@ -258,11 +310,13 @@ int64_t oracle_kv_quant_append(const uint16_t *x, int64_t n, const int32_t *slot
  * Usable entries: 0 <= t < seq_lens[b], t/64 < max_pages and
  * 0 <= page_table[b][t/64] < num_pages [P1, the -1 entries of short
  * contexts].  out is [B,H,512], lse is [B,H], both fp64. */
-void oracle_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int64_t num_pages,
-                              const int32_t *page_table, int32_t max_pages,
-                              const int32_t *seq_lens, const int32_t *topk, int32_t batch,
-                              int32_t heads, int32_t topk_len, double softmax_scale,
-                              double *out, double *lse, int nthreads)
+typedef void (*dequant_fn)(const uint8_t *row, double *k);
+
+static void decode_rows(const uint16_t *q, const uint8_t *cache, int row_bytes, dequant_fn dequant,
+                        int64_t num_pages, const int32_t *page_table, int32_t max_pages,
+                        const int32_t *seq_lens, const int32_t *topk, int32_t batch, int32_t heads,
+                        int32_t topk_len, double softmax_scale, double *out, double *lse,
+                        int nthreads)
 {
 #ifdef _OPENMP
     if (nthreads > 0)
@@ -281,8 +335,8 @@ void oracle_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int64_t n
             int64_t page = page_table[(int64_t)b * max_pages + t / PAGE_ROWS];
             if (page < 0 || page >= num_pages)
                 continue;
-            const uint8_t *row = cache + (page * PAGE_ROWS + t % PAGE_ROWS) * ROW_BYTES;
-            oracle_dequant_row(row, k + n * DIM);
+            const uint8_t *row = cache + (page * PAGE_ROWS + t % PAGE_ROWS) * row_bytes;
+            dequant(row, k + n * DIM);
             ++n;
         }
         int32_t h;
@@ -327,5 +381,29 @@ void oracle_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int64_t n
     free(k);
 }
 
+/* Decode over the NVFP4 cache [num_pages][64][352]. */
+void oracle_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int64_t num_pages,
+                              const int32_t *page_table, int32_t max_pages,
+                              const int32_t *seq_lens, const int32_t *topk, int32_t batch,
+                              int32_t heads, int32_t topk_len, double softmax_scale,
+                              double *out, double *lse, int nthreads)
+{
+    decode_rows(q, cache, ROW_BYTES, oracle_dequant_row, num_pages, page_table, max_pages,
+                seq_lens, topk, batch, heads, topk_len, softmax_scale, out, lse, nthreads);
+}
+
+/* The same decode over the lean FP8 cache [num_pages][64][576]. */
+void oracle_sparse_mla_decode_fp8(const uint16_t *q, const uint8_t *cache, int64_t num_pages,
+                                  const int32_t *page_table, int32_t max_pages,
+                                  const int32_t *seq_lens, const int32_t *topk, int32_t batch,
+                                  int32_t heads, int32_t topk_len, double softmax_scale,
+                                  double *out, double *lse, int nthreads)
+{
+    decode_rows(q, cache, FP8_ROW_BYTES, oracle_dequant_row_fp8, num_pages, page_table,
+                max_pages, seq_lens, topk, batch, heads, topk_len, softmax_scale, out, lse,
+                nthreads);
+}
+
 int oracle_row_bytes(void) { return ROW_BYTES; }
+int oracle_fp8_row_bytes(void) { return FP8_ROW_BYTES; }
 int oracle_page_rows(void) { return PAGE_ROWS; }
