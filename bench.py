@@ -9,6 +9,7 @@ Infinity Cache.
 
 Prints ONE JSON line (metric, value = effective KV GB/s over the step, ...,
 roofline of the decode kernel, cpu_baseline of the oracle on host cores).
+`--format fp8` runs the same step over the lean FP8 cache (576-byte rows).
 """
 from __future__ import annotations
 
@@ -28,8 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0    # MI355X dense FP16/BF16 matrix, published
-ROW_BYTES = 352
-APPEND_BYTES_PER_ROW = 576 * 2 + ROW_BYTES     # BF16 row read + NVFP4 row written
+ROW_BYTES = {"nvfp4": 352, "fp8": 576}          # bytes of one cache row
 FLOPS_PER_HEAD_ROW = 2 * 576 + 2 * 512         # score + value contraction
 CACHE_BYTES_MALL = 256 << 20
 
@@ -48,6 +48,10 @@ def kernel_source_hash() -> str:
         with open(os.path.join(ROOT, "sparse_mla_decode_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def traffic_key(workload: str, fmt: str) -> str:
+    return workload if fmt == "nvfp4" else workload + "-" + fmt
 
 
 def measured_traffic(workload: str):
@@ -133,7 +137,7 @@ def summarize_counters(fetch_dir, write_dir, workload):
     return "\n".join(lines)
 
 
-def cpu_baseline(w, seed, lens, tk_np, qbits, budget_s, dev):
+def cpu_baseline(w, seed, lens, tk_np, qbits, budget_s, dev, fmt):
     """Time the oracle's decode on host cores over as many sequences as fit in
     roughly budget_s seconds (at least one)."""
     import torch
@@ -147,9 +151,11 @@ def cpu_baseline(w, seed, lens, tk_np, qbits, budget_s, dev):
         sel = tk_np[b][tk_np[b] >= 0].astype(np.int64)
         sel = sel[sel < lens[b]]
         n = sel.size
-        rows = oracle.quant_rows(wl.bf16_bits(wl.rows_at(w, seed, b, sel, device=dev)))
-        mini = np.zeros(((max(n, 1) + 63) // 64, 64, 352), dtype=np.uint8)
-        mini.reshape(-1, 352)[:n] = rows
+        quant = oracle.quant_rows if fmt == "nvfp4" else oracle.quant_rows_fp8
+        rb = ROW_BYTES[fmt]
+        rows = quant(wl.bf16_bits(wl.rows_at(w, seed, b, sel, device=dev)))
+        mini = np.zeros(((max(n, 1) + 63) // 64, 64, rb), dtype=np.uint8)
+        mini.reshape(-1, rb)[:n] = rows
         pt = np.arange(mini.shape[0], dtype=np.int32)[None]
         t0 = time.perf_counter()
         oracle.sparse_mla_decode(qbits[b:b + 1], mini, pt, np.array([n]),
@@ -157,7 +163,7 @@ def cpu_baseline(w, seed, lens, tk_np, qbits, budget_s, dev):
                                  nthreads=cores)
         t_used += time.perf_counter() - t0
         done += 1
-        kv_bytes += n * ROW_BYTES
+        kv_bytes += n * rb
         if t_used >= budget_s:
             break
     gbps = kv_bytes / t_used / 1e9
@@ -174,6 +180,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="allheads")
+    ap.add_argument("--format", choices=("nvfp4", "fp8"), default="nvfp4",
+                    help="cache row format: NVFP4 (352 B) or lean FP8 (576 B)")
     ap.add_argument("--sets", type=int, default=0, help="rotating (q, top-k) sets (0 = auto)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -190,7 +198,8 @@ def main():
         print(summarize_kernel_stats(args.summarize_kernel_stats))
         return
     if args.summarize_counters:
-        print(summarize_counters(*args.summarize_counters, args.workload))
+        print(summarize_counters(*args.summarize_counters,
+                                 traffic_key(args.workload, args.format)))
         return
 
     if args.gpus != 1:
@@ -205,11 +214,14 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = wl.WORKLOADS[args.workload]
+    fmt = args.format
+    rbytes = ROW_BYTES[fmt]
+    append_bytes_per_row = 576 * 2 + rbytes      # BF16 row read + cache row written
     seed = args.seed
     lens = wl.context_lengths(w, seed)
     pt_np, num_pages = wl.build_page_table(w, lens, seed)
-    log("workload %s: %s; cache %d pages (%.2f GB)" % (w.name, w.desc, num_pages,
-                                                       num_pages * 22528 / 1e9))
+    log("workload %s (%s rows): %s; cache %d pages (%.2f GB)" % (
+        w.name, fmt, w.desc, num_pages, num_pages * 64 * rbytes / 1e9))
     if args.calibrate_copy:
         a = torch.ones(CALIB_FLOATS, dtype=torch.float32, device=dev)
         b_ = torch.empty_like(a)
@@ -218,8 +230,11 @@ def main():
         torch.cuda.synchronize()
         del a, b_
 
-    cache = torch.zeros((num_pages, 64, 352), dtype=torch.uint8, device=dev)
-    append = lambda rows, slots: smla.kv_quant_append(rows, slots, cache)
+    cache = torch.zeros((num_pages, 64, rbytes), dtype=torch.uint8, device=dev)
+    append_fn = smla.kv_quant_append if fmt == "nvfp4" else smla.kv_quant_append_fp8
+    decode_fn = smla.sparse_mla_decode if fmt == "nvfp4" else smla.sparse_mla_decode_fp8
+    ws_fn = smla.decode_workspace_bytes if fmt == "nvfp4" else smla.decode_workspace_bytes_fp8
+    append = lambda rows, slots: append_fn(rows, slots, cache)
     t0 = time.time()
     wl.fill_cache(w, seed, lens, pt_np, append, dev, tail=w.append_tail)
     # the step's append: the newest min(tail, L) tokens (ragged, million) or
@@ -232,7 +247,7 @@ def main():
 
     pt = torch.as_tensor(pt_np, device=dev)
     sl = torch.as_tensor(lens.astype(np.int32), device=dev)
-    per_call_bytes = int(sum(min(w.topk, int(L)) for L in lens)) * ROW_BYTES
+    per_call_bytes = int(sum(min(w.topk, int(L)) for L in lens)) * rbytes
     sets = args.sets or max(4, math.ceil(2 * CACHE_BYTES_MALL / max(per_call_bytes, 1)) + 1)
     qs, tks, nvalid = [], [], []
     for s in range(sets):
@@ -242,7 +257,7 @@ def main():
         qs.append(wl.queries(w, seed, set_id=s, device=dev))
     out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device=dev)
-    ws_bytes = smla.decode_workspace_bytes(w.batch, w.heads, w.topk)
+    ws_bytes = ws_fn(w.batch, w.heads, w.topk)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     log("%d rotating sets, %.1f MB of selected rows each" % (sets, per_call_bytes / 1e6))
 
@@ -250,11 +265,10 @@ def main():
         s = i % sets
         if ev is not None:
             ev[0].record()
-        smla.kv_quant_append(step_rows, step_slots, cache)
+        append_fn(step_rows, step_slots, cache)
         if ev is not None:
             ev[1].record()
-        smla.sparse_mla_decode(qs[s], cache, pt, sl, tks[s], w.softmax_scale, out=out,
-                               lse=lse, workspace=ws)
+        decode_fn(qs[s], cache, pt, sl, tks[s], w.softmax_scale, out=out, lse=lse, workspace=ws)
         if ev is not None:
             ev[2].record()
 
@@ -275,16 +289,16 @@ def main():
 
     # algorithmic work per step (mean over the sets the timed steps used)
     used = [(args.warmup + i) % sets for i in range(args.steps)]
-    dec_bytes = float(np.mean([nvalid[s] for s in used])) * ROW_BYTES
-    app_bytes = step_rows.shape[0] * APPEND_BYTES_PER_ROW
+    dec_bytes = float(np.mean([nvalid[s] for s in used])) * rbytes
+    app_bytes = step_rows.shape[0] * append_bytes_per_row
     dec_flops = float(np.mean([nvalid[s] for s in used])) * w.heads * FLOPS_PER_HEAD_ROW
     value = (dec_bytes + app_bytes) / (ms_per_step * 1e-3) / 1e9
     dec_s = float(dec_ms.mean()) * 1e-3
     dec_gbps = dec_bytes / dec_s / 1e9
     dec_tflops = dec_flops / dec_s / 1e12
-    ai = w.heads * FLOPS_PER_HEAD_ROW / ROW_BYTES
+    ai = w.heads * FLOPS_PER_HEAD_ROW / rbytes
     ridge = MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(traffic_key(w.name, fmt))
     if ai >= ridge:
         roof = {"bound": "mfma", "achieved": round(dec_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(dec_tflops / MFMA_F16_PEAK_TFLOPS, 4),
@@ -294,7 +308,9 @@ def main():
                 "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
 
     result = {
-        "metric": "sparse NVFP4-MLA decode: effective KV GB/s (% HBM peak) and queries/sec",
+        "metric": ("sparse NVFP4-MLA decode: effective KV GB/s (% HBM peak) and queries/sec"
+                   if fmt == "nvfp4" else
+                   "sparse MLA decode over lean FP8 rows: effective KV GB/s and queries/sec"),
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -306,7 +322,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "topk": w.topk,
+        "config": {"workload": w.name, "row_format": fmt, "batch": w.batch, "heads": w.heads, "topk": w.topk,
                    "context": int(lens.max()) if w.ctx == 0 else w.ctx,
                    "append_rows_per_step": int(step_rows.shape[0]),
                    "rotating_sets": sets, "desc": w.desc},
@@ -322,7 +338,8 @@ def main():
         tk0 = wl.topk_indices(w, lens, seed, set_id=0)
         qbits = wl.bf16_bits(qs[0])
         log("timing the oracle on host cores (budget %.0f s)" % args.cpu_budget)
-        result["cpu_baseline"] = cpu_baseline(w, seed, lens, tk0, qbits, args.cpu_budget, dev)
+        result["cpu_baseline"] = cpu_baseline(w, seed, lens, tk0, qbits, args.cpu_budget, dev,
+                                              fmt)
     print(json.dumps(result), flush=True)
 
 

@@ -7,6 +7,9 @@
  *   smla_kv_quant_append   BF16 KV rows -> 352-byte NVFP4 rows in the paged cache
  *   smla_sparse_mla_decode q, cache, page table, top-k indices -> out, lse
  *
+ * and the same pair over the lean FP8 row that the pages compare NVFP4 with
+ * (smla_kv_quant_append_fp8, smla_sparse_mla_decode_fp8; see the end).
+ *
  * Sources (page titles; no other document is needed to read this header):
  *   [P1] "Prime Inference: serving GLM-5.3 to agents is a KV-cache problem",
  *        section "Four bits per latent value: where 352 comes from" (row bytes:
@@ -65,6 +68,7 @@ extern "C" {
 #define SMLA_ROW_BYTES 352
 #define SMLA_PAGE_ROWS 64
 #define SMLA_PAGE_BYTES (SMLA_PAGE_ROWS * SMLA_ROW_BYTES)
+#define SMLA_FP8_ROW_BYTES 576
 #define SMLA_MAX_TOPK 2048
 
 enum {
@@ -148,6 +152,34 @@ int smla_sparse_mla_decode(const void *q_bf16, const uint8_t *cache, int64_t num
                            int32_t batch, int32_t heads, int32_t topk, float softmax_scale,
                            float *out, float *lse, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/*
+ * ---- Lean FP8 rows [P1 row-bytes table: FP8 row = 512 + 64 bytes] ----
+ *
+ * Row format (one token, 576 bytes): the 576 values (latent 0..511, then
+ * rope 0..63) as OCP FP8 E4M3 bytes in dim order, no scale, each the E4M3
+ * value nearest the input (ties to even, saturating at +-448, sign copied):
+ * the rule of the NVFP4 row's rope bytes.  A page is 64 rows (36,864 bytes);
+ * the cache is [num_pages][64][576] bytes.  K is the 576 decoded values, V
+ * the first 512.
+ *
+ * The three calls below take the same arguments, with the same meaning,
+ * conventions and errors, as their NVFP4 counterparts above; only the row
+ * format of `cache` differs.  smla_decode_workspace_bytes_fp8 may differ from
+ * the NVFP4 figure for the same shape (an FP8 split scans at most 1024
+ * entries).
+ */
+int smla_kv_quant_append_fp8(const void *rows_bf16, int64_t n, const int32_t *slot_mapping,
+                             uint8_t *cache, int64_t num_pages, void *stream);
+
+size_t smla_decode_workspace_bytes_fp8(int32_t batch, int32_t heads, int32_t topk);
+
+int smla_sparse_mla_decode_fp8(const void *q_bf16, const uint8_t *cache, int64_t num_pages,
+                               const int32_t *page_table, int32_t max_pages,
+                               const int32_t *seq_lens, const int32_t *topk_indices,
+                               int32_t batch, int32_t heads, int32_t topk, float softmax_scale,
+                               float *out, float *lse, void *workspace, size_t workspace_bytes,
+                               void *stream);
 
 #ifdef __cplusplus
 }

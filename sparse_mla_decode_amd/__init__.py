@@ -9,6 +9,8 @@ not been built, importing this package raises.
         rows [n,576] bf16, slot_mapping [n] int32, cache [P,64,352] uint8 (in place)
     sparse_mla_decode(q, cache, page_table, seq_lens, topk, softmax_scale)
         -> (out [B,H,512] fp32, lse [B,H] fp32)
+    kv_quant_append_fp8, sparse_mla_decode_fp8
+        the same over the lean FP8 row: cache [P,64,576] uint8
 """
 from __future__ import annotations
 
@@ -25,6 +27,7 @@ LATENT = 512
 ROPE = 64
 DIM = 576
 ROW_BYTES = 352
+FP8_ROW_BYTES = 576
 PAGE_ROWS = 64
 MAX_TOPK = 2048
 
@@ -35,7 +38,8 @@ ERRORS = {
 
 # exported symbols, in the order include/smla.h declares them
 EXPORTS = ("smla_strerror", "smla_version", "smla_kv_quant_append",
-           "smla_decode_workspace_bytes", "smla_sparse_mla_decode")
+           "smla_decode_workspace_bytes", "smla_sparse_mla_decode", "smla_kv_quant_append_fp8",
+           "smla_decode_workspace_bytes_fp8", "smla_sparse_mla_decode_fp8")
 
 
 class SmlaError(RuntimeError):
@@ -58,13 +62,16 @@ def _load() -> ctypes.CDLL:
     lib.smla_strerror.restype = ctypes.c_char_p
     lib.smla_version.argtypes = []
     lib.smla_version.restype = ctypes.c_int
-    lib.smla_kv_quant_append.argtypes = [P, i64, P, P, i64, P]
-    lib.smla_kv_quant_append.restype = ctypes.c_int
-    lib.smla_decode_workspace_bytes.argtypes = [i32, i32, i32]
-    lib.smla_decode_workspace_bytes.restype = sz
-    lib.smla_sparse_mla_decode.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, f32,
-                                           P, P, P, sz, P]
-    lib.smla_sparse_mla_decode.restype = ctypes.c_int
+    for sfx in ("", "_fp8"):
+        fn = getattr(lib, "smla_kv_quant_append" + sfx)
+        fn.argtypes = [P, i64, P, P, i64, P]
+        fn.restype = ctypes.c_int
+        fn = getattr(lib, "smla_decode_workspace_bytes" + sfx)
+        fn.argtypes = [i32, i32, i32]
+        fn.restype = sz
+        fn = getattr(lib, "smla_sparse_mla_decode" + sfx)
+        fn.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, f32, P, P, P, sz, P]
+        fn.restype = ctypes.c_int
     return lib
 
 
@@ -108,6 +115,10 @@ def decode_workspace_bytes(batch: int, heads: int, topk: int) -> int:
     return int(lib.smla_decode_workspace_bytes(batch, heads, topk))
 
 
+def decode_workspace_bytes_fp8(batch: int, heads: int, topk: int) -> int:
+    return int(lib.smla_decode_workspace_bytes_fp8(batch, heads, topk))
+
+
 def workspace_for(device: torch.device, nbytes: int, stream=None) -> torch.Tensor:
     """A workspace of at least nbytes, cached per (device, stream)."""
     key = (device.index, _stream_ptr(device, stream))
@@ -119,26 +130,33 @@ def workspace_for(device: torch.device, nbytes: int, stream=None) -> torch.Tenso
         return ws
 
 
-def kv_quant_append(rows: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tensor,
-                    stream=None) -> None:
-    """Quantise BF16 rows [n,576] into cache slots (page*64 + row) of cache [P,64,352]."""
+def _append(rows, slot_mapping, cache, stream, row_bytes, fn):
     _req(cache, "cache", torch.uint8, 3)
     dev = cache.device
     _req(rows, "rows", torch.bfloat16, 2, dev)
     _req(slot_mapping, "slot_mapping", torch.int32, 1, dev)
     if rows.shape[1] != DIM or slot_mapping.shape[0] != rows.shape[0]:
         raise ValueError("rows must be [n,576] and slot_mapping [n]")
-    if tuple(cache.shape[1:]) != (PAGE_ROWS, ROW_BYTES):
-        raise ValueError("cache must be [num_pages,64,352]")
-    _check(lib.smla_kv_quant_append(rows.data_ptr(), rows.shape[0], slot_mapping.data_ptr(),
-                                    cache.data_ptr(), cache.shape[0], _stream_ptr(dev, stream)))
+    if tuple(cache.shape[1:]) != (PAGE_ROWS, row_bytes):
+        raise ValueError("cache must be [num_pages,64,%d]" % row_bytes)
+    _check(fn(rows.data_ptr(), rows.shape[0], slot_mapping.data_ptr(), cache.data_ptr(),
+              cache.shape[0], _stream_ptr(dev, stream)))
 
 
-def sparse_mla_decode(q: torch.Tensor, cache: torch.Tensor, page_table: torch.Tensor,
-                      seq_lens: torch.Tensor, topk: torch.Tensor, softmax_scale: float,
-                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-                      workspace: torch.Tensor | None = None, stream=None):
-    """Sparse MLA decode; returns (out [B,H,512] fp32, lse [B,H] fp32)."""
+def kv_quant_append(rows: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tensor,
+                    stream=None) -> None:
+    """Quantise BF16 rows [n,576] into cache slots (page*64 + row) of cache [P,64,352]."""
+    _append(rows, slot_mapping, cache, stream, ROW_BYTES, lib.smla_kv_quant_append)
+
+
+def kv_quant_append_fp8(rows: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tensor,
+                        stream=None) -> None:
+    """Quantise BF16 rows [n,576] into lean FP8 rows of cache [P,64,576]."""
+    _append(rows, slot_mapping, cache, stream, FP8_ROW_BYTES, lib.smla_kv_quant_append_fp8)
+
+
+def _decode(q, cache, page_table, seq_lens, topk, softmax_scale, out, lse, workspace, stream,
+            row_bytes, fn, ws_fn):
     _req(cache, "cache", torch.uint8, 3)
     dev = cache.device
     _req(q, "q", torch.bfloat16, 3, dev)
@@ -148,8 +166,8 @@ def sparse_mla_decode(q: torch.Tensor, cache: torch.Tensor, page_table: torch.Te
     B, H, D = q.shape
     if D != DIM:
         raise ValueError("q must be [B,H,576]")
-    if tuple(cache.shape[1:]) != (PAGE_ROWS, ROW_BYTES):
-        raise ValueError("cache must be [num_pages,64,352]")
+    if tuple(cache.shape[1:]) != (PAGE_ROWS, row_bytes):
+        raise ValueError("cache must be [num_pages,64,%d]" % row_bytes)
     if page_table.shape[0] != B or seq_lens.shape[0] != B or topk.shape[0] != B:
         raise ValueError("page_table, seq_lens and topk need one row per sequence")
     K = topk.shape[1]
@@ -161,14 +179,32 @@ def sparse_mla_decode(q: torch.Tensor, cache: torch.Tensor, page_table: torch.Te
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     else:
         _req(lse, "lse", torch.float32, 2, dev)
-    need = decode_workspace_bytes(B, H, K)
+    need = int(ws_fn(B, H, K))
     if workspace is None and need > 0:
         workspace = workspace_for(dev, need, stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.smla_sparse_mla_decode(
-        q.data_ptr(), cache.data_ptr(), cache.shape[0], page_table.data_ptr(),
-        page_table.shape[1], seq_lens.data_ptr(), topk.data_ptr(), B, H, K,
-        float(softmax_scale), out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes,
-        _stream_ptr(dev, stream)))
+    _check(fn(q.data_ptr(), cache.data_ptr(), cache.shape[0], page_table.data_ptr(),
+              page_table.shape[1], seq_lens.data_ptr(), topk.data_ptr(), B, H, K,
+              float(softmax_scale), out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes,
+              _stream_ptr(dev, stream)))
     return out, lse
+
+
+def sparse_mla_decode(q: torch.Tensor, cache: torch.Tensor, page_table: torch.Tensor,
+                      seq_lens: torch.Tensor, topk: torch.Tensor, softmax_scale: float,
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None):
+    """Sparse MLA decode over cache [P,64,352]; returns (out [B,H,512] fp32, lse [B,H] fp32)."""
+    return _decode(q, cache, page_table, seq_lens, topk, softmax_scale, out, lse, workspace,
+                   stream, ROW_BYTES, lib.smla_sparse_mla_decode, lib.smla_decode_workspace_bytes)
+
+
+def sparse_mla_decode_fp8(q: torch.Tensor, cache: torch.Tensor, page_table: torch.Tensor,
+                          seq_lens: torch.Tensor, topk: torch.Tensor, softmax_scale: float,
+                          out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None, stream=None):
+    """The same decode over the lean FP8 cache [P,64,576]."""
+    return _decode(q, cache, page_table, seq_lens, topk, softmax_scale, out, lse, workspace,
+                   stream, FP8_ROW_BYTES, lib.smla_sparse_mla_decode_fp8,
+                   lib.smla_decode_workspace_bytes_fp8)

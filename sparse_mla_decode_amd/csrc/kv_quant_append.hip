@@ -12,6 +12,11 @@
 // values 2j, 2j+1.  A 256-thread workgroup quantises 8 rows.  The kernel is
 // HBM-bound (1152 B read and 352 B written per row); loads of a row are one
 // contiguous 1 KiB sweep across its 32 lanes.
+//
+// kv_quant_append_fp8 writes the lean FP8 row of the same section's byte
+// table instead: the 576 values as E4M3 bytes in dim order, no scale, each
+// the E4M3 value nearest the input (the rope rule).  36 lanes per row, lane j
+// owns values 16j .. 16j+15; a 288-thread workgroup quantises 8 rows.
 #include "smla_internal.h"
 
 namespace smla {
@@ -128,7 +133,39 @@ __global__ __launch_bounds__(256) void kv_quant_append_kernel(const uint16_t *__
     *reinterpret_cast<uint16_t *>(dst + kRopeOff + 2 * j) = (uint16_t)(c0 | (c1 << 8));
 }
 
+__global__ __launch_bounds__(288) void kv_quant_append_fp8_kernel(const uint16_t *__restrict__ rows,
+                                                                   int64_t n,
+                                                                   const int32_t *__restrict__ slots,
+                                                                   uint8_t *__restrict__ cache,
+                                                                   int64_t num_slots) {
+    const int64_t row = (int64_t)blockIdx.x * 8 + threadIdx.x / 36;
+    const int j = threadIdx.x % 36;
+    if (row >= n) return;
+    const int64_t slot = slots[row];
+    if (slot < 0 || slot >= num_slots) return;
+    const uint4 lo = *reinterpret_cast<const uint4 *>(rows + row * kDim + 16 * j);
+    const uint4 hi = *reinterpret_cast<const uint4 *>(rows + row * kDim + 16 * j + 8);
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    uint32_t b[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t c0 = e4m3_nearest(__uint_as_float(w[i] << 16));
+        const uint32_t c1 = e4m3_nearest(__uint_as_float(w[i] & 0xFFFF0000u));
+        b[i >> 1] |= (c0 | (c1 << 8)) << (16 * (i & 1));
+    }
+    *reinterpret_cast<uint4 *>(cache + slot * kFp8RowBytes + 16 * j) = make_uint4(b[0], b[1], b[2], b[3]);
+}
+
 }  // namespace
+
+hipError_t launch_kv_quant_append_fp8(const uint16_t *rows, int64_t n, const int32_t *slots,
+                                      uint8_t *cache, int64_t num_pages, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 7) / 8;
+    hipLaunchKernelGGL(kv_quant_append_fp8_kernel, dim3((unsigned)blocks), dim3(288), 0, stream,
+                       rows, n, slots, cache, num_pages * kPageRows);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_quant_append(const uint16_t *rows, int64_t n, const int32_t *slots,
                                   uint8_t *cache, int64_t num_pages, hipStream_t stream) {

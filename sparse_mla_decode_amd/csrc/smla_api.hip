@@ -43,10 +43,14 @@ const char *smla_strerror(int code) {
     }
 }
 
-int smla_version(void) { return 100; }
+int smla_version(void) { return 101; }
 
-int smla_kv_quant_append(const void *rows_bf16, int64_t n, const int32_t *slot_mapping,
-                         uint8_t *cache, int64_t num_pages, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int append_rows(const void *rows_bf16, int64_t n, const int32_t *slot_mapping, uint8_t *cache,
+                int64_t num_pages, void *stream, smla::RowFormat fmt) {
     if (n < 0 || n > INT32_MAX) return SMLA_ERR_SHAPE;
     if (num_pages < 1 || num_pages > ((int64_t)1 << 25)) return SMLA_ERR_SHAPE;
     if (n == 0) return SMLA_OK;
@@ -55,25 +59,25 @@ int smla_kv_quant_append(const void *rows_bf16, int64_t n, const int32_t *slot_m
         return SMLA_ERR_ALIGN;
     const int dev = device_ok();
     if (dev != SMLA_OK) return dev;
-    const hipError_t e = smla::launch_kv_quant_append(
-        static_cast<const uint16_t *>(rows_bf16), n, slot_mapping, cache, num_pages,
-        static_cast<hipStream_t>(stream));
+    const uint16_t *rows = static_cast<const uint16_t *>(rows_bf16);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t e =
+        fmt == smla::kFmtFp8 ? smla::launch_kv_quant_append_fp8(rows, n, slot_mapping, cache, num_pages, st)
+                             : smla::launch_kv_quant_append(rows, n, slot_mapping, cache, num_pages, st);
     return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
-size_t smla_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t topk) {
+size_t workspace_bytes(int32_t batch, int32_t heads, int32_t topk, smla::RowFormat fmt) {
     if (batch < 1 || batch > 65535 || (heads != 16 && heads != 64) || topk < 1 ||
         topk > SMLA_MAX_TOPK)
         return 0;
-    return smla::plan_decode(batch, heads, topk).workspace_bytes;
+    return smla::plan_decode(batch, heads, topk, fmt).workspace_bytes;
 }
 
-int smla_sparse_mla_decode(const void *q_bf16, const uint8_t *cache, int64_t num_pages,
-                           const int32_t *page_table, int32_t max_pages,
-                           const int32_t *seq_lens, const int32_t *topk_indices,
-                           int32_t batch, int32_t heads, int32_t topk, float softmax_scale,
-                           float *out, float *lse, void *workspace, size_t workspace_bytes,
-                           void *stream) {
+int decode(const void *q_bf16, const uint8_t *cache, int64_t num_pages, const int32_t *page_table,
+           int32_t max_pages, const int32_t *seq_lens, const int32_t *topk_indices, int32_t batch,
+           int32_t heads, int32_t topk, float softmax_scale, float *out, float *lse,
+           void *workspace, size_t workspace_bytes, void *stream, smla::RowFormat fmt) {
     if (heads != 16 && heads != 64) return SMLA_ERR_UNSUPPORTED;
     if (batch < 1 || batch > 65535 || topk < 1 || topk > SMLA_MAX_TOPK || max_pages < 1 ||
         num_pages < 1 || num_pages > ((int64_t)1 << 25))
@@ -83,7 +87,7 @@ int smla_sparse_mla_decode(const void *q_bf16, const uint8_t *cache, int64_t num
     if (!aligned(q_bf16, 16) || !aligned(out, 16) || !aligned(cache, 256) || !aligned(lse, 4) ||
         !aligned(page_table, 4) || !aligned(seq_lens, 4) || !aligned(topk_indices, 4))
         return SMLA_ERR_ALIGN;
-    const smla::DecodePlan plan = smla::plan_decode(batch, heads, topk);
+    const smla::DecodePlan plan = smla::plan_decode(batch, heads, topk, fmt);
     if (plan.workspace_bytes > 0) {
         if (!workspace || workspace_bytes < plan.workspace_bytes) return SMLA_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return SMLA_ERR_ALIGN;
@@ -92,9 +96,53 @@ int smla_sparse_mla_decode(const void *q_bf16, const uint8_t *cache, int64_t num
     if (dev != SMLA_OK) return dev;
     const hipError_t e = smla::launch_sparse_mla_decode(
         static_cast<const uint16_t *>(q_bf16), cache, num_pages, page_table, max_pages, seq_lens,
-        topk_indices, batch, heads, topk, softmax_scale, out, lse, workspace, plan,
+        topk_indices, batch, heads, topk, softmax_scale, out, lse, workspace, plan, fmt,
         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int smla_kv_quant_append(const void *rows_bf16, int64_t n, const int32_t *slot_mapping,
+                         uint8_t *cache, int64_t num_pages, void *stream) {
+    return append_rows(rows_bf16, n, slot_mapping, cache, num_pages, stream, smla::kFmtNvfp4);
+}
+
+size_t smla_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t topk) {
+    return workspace_bytes(batch, heads, topk, smla::kFmtNvfp4);
+}
+
+int smla_sparse_mla_decode(const void *q_bf16, const uint8_t *cache, int64_t num_pages,
+                           const int32_t *page_table, int32_t max_pages,
+                           const int32_t *seq_lens, const int32_t *topk_indices,
+                           int32_t batch, int32_t heads, int32_t topk, float softmax_scale,
+                           float *out, float *lse, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    return decode(q_bf16, cache, num_pages, page_table, max_pages, seq_lens, topk_indices, batch,
+                  heads, topk, softmax_scale, out, lse, workspace, workspace_bytes, stream,
+                  smla::kFmtNvfp4);
+}
+
+int smla_kv_quant_append_fp8(const void *rows_bf16, int64_t n, const int32_t *slot_mapping,
+                             uint8_t *cache, int64_t num_pages, void *stream) {
+    return append_rows(rows_bf16, n, slot_mapping, cache, num_pages, stream, smla::kFmtFp8);
+}
+
+size_t smla_decode_workspace_bytes_fp8(int32_t batch, int32_t heads, int32_t topk) {
+    return workspace_bytes(batch, heads, topk, smla::kFmtFp8);
+}
+
+int smla_sparse_mla_decode_fp8(const void *q_bf16, const uint8_t *cache, int64_t num_pages,
+                               const int32_t *page_table, int32_t max_pages,
+                               const int32_t *seq_lens, const int32_t *topk_indices,
+                               int32_t batch, int32_t heads, int32_t topk, float softmax_scale,
+                               float *out, float *lse, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+    return decode(q_bf16, cache, num_pages, page_table, max_pages, seq_lens, topk_indices, batch,
+                  heads, topk, softmax_scale, out, lse, workspace, workspace_bytes, stream,
+                  smla::kFmtFp8);
 }
 
 }  // extern "C"

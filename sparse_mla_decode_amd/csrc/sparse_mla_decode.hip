@@ -47,6 +47,8 @@
 //     workgroup, an L2 writeback, which costs more than the launch).
 #include "smla_internal.h"
 
+#include <type_traits>
+
 namespace smla {
 namespace {
 
@@ -61,18 +63,38 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kThreads = 512;                   // 4 score waves + 4 value waves, two per SIMD
 constexpr int kTile = 64;                       // selected rows per tile (16 per wave)
-constexpr int kNBuf = 5;                        // ring of packed tiles in LDS
-constexpr int kTileBytes = kTile * kRowBytes;   // 22,528
-constexpr int kDmaPerTile = kTileBytes / 1024;  // wave-wide 16-byte loads per tile (22)
 constexpr int kPStride = kTile + 8;             // f16 per softmax-weight row (144 B)
 constexpr int kSStride = kTile + 8;             // f16 per scale-table row (144 B)
 constexpr int kKSteps = kDim / 32;              // 18 score steps of 32
 constexpr float kSlack = 8.0f;                  // log2 headroom before the running max moves
 constexpr int kMaxSplits = 16;
-static_assert(kTileBytes % 1024 == 0, "a tile must be whole wave-wide loads");
-static_assert(kDmaPerTile > 16 && kDmaPerTile <= 24, "2 or 3 loads per wave per tile");
-static_assert(kNBuf >= 5 && 2 * kKSteps * 1024 <= 2 * kTileBytes,
-              "the query of 32 heads is staged in ring slots 3 and 4");
+
+// The tile ring for each row format: row bytes, where the rope bytes start,
+// ring slots, and how far ahead the loads run (tile s + kAhead is loaded in
+// step s, into the slot of tile s - 2).  An FP8 tile is 36 KB, so its ring
+// has four slots (one step of slack for the loads instead of two) and a
+// split scans at most 1024 entries (4 KB of row ids).
+template <int FMT> struct Ring;
+template <> struct Ring<kFmtNvfp4> {
+    static constexpr int kRow = kRowBytes;      // 352
+    static constexpr int kRopeAt = kRopeOff;    // 288
+    static constexpr int kNBuf = 5;
+    static constexpr int kAhead = 3;
+    static constexpr int kMaxPerSplit = kMaxTopk;
+};
+template <> struct Ring<kFmtFp8> {
+    static constexpr int kRow = kFp8RowBytes;   // 576
+    static constexpr int kRopeAt = kLatent;     // 512
+    static constexpr int kNBuf = 4;
+    static constexpr int kAhead = 2;
+    static constexpr int kMaxPerSplit = 1024;
+};
+
+// FP8 tiles are stored with the latent 16-byte pieces of row r permuted by
+// XOR with swz(r) (the rope pieces stay in place): the value waves' 8-byte
+// transposing reads of 8 rows x 4 column windows then spread over all LDS
+// banks instead of the two that a 576-byte row stride leaves them.
+__device__ __forceinline__ int fp8_swz(int r) { return ((r >> 1) & 3) << 1; }
 
 __device__ __forceinline__ half8_t join(half2_t a, half2_t b, half2_t c, half2_t d) {
     half8_t r;
@@ -152,7 +174,7 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
     }
 }
 
-template <int MB>
+template <int MB, int FMT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ cache,
                               int64_t num_pages, const int32_t *__restrict__ page_table,
@@ -162,10 +184,23 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                               _Float16 *__restrict__ part_o, float *__restrict__ part_ml,
                               int32_t batch, int32_t groups, int32_t splits, int32_t per_split) {
     constexpr int HG = 16 * MB;  // heads of this workgroup
+    using R = Ring<FMT>;
+    constexpr bool kFp8 = FMT == kFmtFp8;
+    constexpr int kNBuf = R::kNBuf;
+    constexpr int kAhead = R::kAhead;
+    constexpr int kRowB = R::kRow;
+    constexpr int kTileBytes = kTile * kRowB;       // 22,528 or 36,864
+    constexpr int kChunks = kRowB / 16;             // 16-byte pieces per row (22 or 36)
+    constexpr int kDmaPerTile = kTileBytes / 1024;  // wave-wide 16-byte loads per tile (22 or 36)
+    constexpr int kMaxDma = (kDmaPerTile + 3) / 4;  // per value wave (6 or 9)
+    static_assert(kTileBytes % 1024 == 0, "a tile must be whole wave-wide loads");
+    static_assert((kNBuf - 3) * kTileBytes >= 2 * kKSteps * 1024,
+                  "the query of 32 heads is staged from ring slot 3 on");
+    static_assert(kNBuf - kAhead == 2, "tile s + kAhead goes into the slot of tile s - 2");
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kNBuf * kTileBytes];
     __shared__ __attribute__((aligned(16))) _Float16 p_lds[2][32 * kPStride];
-    __shared__ __attribute__((aligned(16))) _Float16 st_lds[2][32 * kSStride];
-    __shared__ uint32_t rowid_lds[kMaxTopk];
+    __shared__ __attribute__((aligned(16))) _Float16 st_lds[kFp8 ? 1 : 2][kFp8 ? 8 : 32 * kSStride];
+    __shared__ uint32_t rowid_lds[R::kMaxPerSplit];
     __shared__ __attribute__((aligned(16))) float red_lds[2][4][32];  // per-wave tile maxima
     __shared__ float alpha_lds[2][32];    // rescale factors when the running max moved
     __shared__ float sum_lds[4][32];
@@ -201,38 +236,41 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         return __builtin_amdgcn_readfirstlane(scan_lds[0] + scan_lds[1] + scan_lds[2] + scan_lds[3]);
     };
     // ---- tile ring, loaded by the value waves: value wave v = w - 4 issues
-    // the wave-wide loads i = v, v+4, ..., v+20 of a tile; load i moves bytes
-    // [1024 i, 1024 i + 1024) of the 64 packed rows, lane l the 16-byte piece
-    // (64 i + l) % 22 of row (64 i + l) / 22.  Slot (tile % kNBuf); the
-    // value waves read tile t in step t + 1, so at step s the loads of tile
-    // s + kNBuf - 2 go into the slot of tile s - 2 ----
-    const int n_dma = (sw + 20 < kDmaPerTile) ? 6 : 5;
-    int dma_row[6], dma_off[6];
+    // the wave-wide loads i = v, v+4, ... of a tile; load i fills LDS bytes
+    // [1024 i, 1024 i + 1024) of the tile, lane l the 16-byte piece
+    // (64 i + l) % kChunks of row (64 i + l) / kChunks (for FP8 the latent
+    // pieces of row r come from piece c ^ fp8_swz(r) of the cache row).
+    // Slot (tile % kNBuf); the value waves read tile t in step t + 1, so at
+    // step s the loads of tile s + kAhead go into the slot of tile s - 2 ----
+    const int n_dma = (kDmaPerTile - sw + 3) / 4;
+    int dma_row[kMaxDma], dma_off[kMaxDma];
 #pragma unroll
-    for (int k = 0; k < 6; ++k) {
+    for (int k = 0; k < kMaxDma; ++k) {
         const int slot = 64 * (sw + 4 * k) + lane;
-        dma_row[k] = min(slot / 22, kTile - 1);
-        dma_off[k] = (slot % 22) * 16;
+        const int r = min(slot / kChunks, kTile - 1);
+        const int c = slot % kChunks;
+        dma_row[k] = r;
+        dma_off[k] = 16 * ((kFp8 && c < kLatent / 16) ? (c ^ fp8_swz(r)) : c);
     }
     const uint32_t ring_addr = (uint32_t)(size_t)(lds_void_t *)ring;
     // the row ids of this wave's loads of tile T, then the loads themselves
     // (split so that the id reads can be issued early)
-    auto tile_rows = [&](int T, uint32_t (&r6)[6]) {
+    auto tile_rows = [&](int T, uint32_t (&rk)[kMaxDma]) {
         const uint32_t *rows = rowid_lds + T * kTile;
 #pragma unroll
-        for (int k = 0; k < 6; ++k) r6[k] = rows[dma_row[k]];
+        for (int k = 0; k < kMaxDma; ++k) rk[k] = rows[dma_row[k]];
     };
-    auto tile_dma = [&](int T, const uint32_t (&r6)[6]) {
+    auto tile_dma = [&](int T, const uint32_t (&rk)[kMaxDma]) {
         const uint32_t dst = ring_addr + (uint32_t)((T % kNBuf) * kTileBytes + sw * 1024);
 #pragma unroll
-        for (int k = 0; k < 6; ++k)
+        for (int k = 0; k < kMaxDma; ++k)
             if (k < n_dma)
-                dma16(cache + (size_t)r6[k] * kRowBytes + dma_off[k], dst + (uint32_t)(k * 4 * 1024));
+                dma16(cache + (size_t)rk[k] * kRowB + dma_off[k], dst + (uint32_t)(k * 4 * 1024));
     };
     auto issue = [&](int T) {
-        uint32_t r6[6];
-        tile_rows(T, r6);
-        tile_dma(T, r6);
+        uint32_t rk[kMaxDma];
+        tile_rows(T, rk);
+        tile_dma(T, rk);
     };
     // flags of the score waves for tile parity pb, as one 16-byte read
     auto read_flags = [&](int pb) {
@@ -247,7 +285,9 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     // tile t is in LDS once at most the loads of the tiles issued after it
     // are outstanding: `after` of them (value waves only)
     auto wait_tile = [&](int after) {
-        if (after == 1) {
+        if (after <= 0) {
+            wait_vmcnt_n<0>();
+        } else if (after == 1 && !kFp8) {
             if (n_dma == 6) wait_vmcnt_n<6>();
             else wait_vmcnt_n<5>();
         } else {
@@ -267,8 +307,8 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         // ...): load i = 18 mb + j puts, for every lane, that lane's A
         // operand of score step j (heads 16 mb ..) into 1 KB of LDS, so each
         // score wave reads its operands back with one linear 16-byte read per
-        // step.  The staging area is ring slots 3 and 4, which take their
-        // first tiles only after the initial barrier.
+        // step.  The staging area starts at ring slot 3, whose first tile is
+        // loaded only after the initial barrier.
         const uint32_t q_lds = ring_addr + 3u * kTileBytes;
         for (int i = sw; i < MB * kKSteps; i += 4) {
             const int mb = i / kKSteps, j = i % kKSteps;
@@ -310,47 +350,76 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 #pragma unroll
             for (int r = 0; r < 4; ++r) m_run[mb][r] = 0.0f;
 
-        // this wave's packed bytes of one tile: 4 x 16 B of nibbles (dims
-        // 128g .. 128g+127), the 8 block scales of those dims, 16 rope bytes
-        struct Packed {
+        // this wave's packed bytes of one tile, dims 128g .. 128g+127 and rope
+        // 16g .. 16g+15: NVFP4 -- 4 x 16 B of nibbles, the 8 block scales, 16
+        // rope bytes; FP8 -- 8 x 16 B of latent bytes, 16 rope bytes
+        struct PackedNvfp4 {
             uint4 nib[4];
             uint2 sc;
             uint4 rope;
         };
-        auto load_packed = [&](int T, Packed &pk) {
-            const uint8_t *rp = ring + (T % kNBuf) * kTileBytes + row * kRowBytes;
+        struct PackedFp8 {
+            uint4 lat[8];
+            uint4 rope;
+        };
+        using Packed = typename std::conditional<kFp8, PackedFp8, PackedNvfp4>::type;
+        // FP8: the byte offsets of this lane's 8 latent pieces within its row
+        // (pieces permuted by fp8_swz(row))
+        int lat_off[8];
 #pragma unroll
-            for (int jp = 0; jp < 4; ++jp)
-                pk.nib[jp] = *reinterpret_cast<const uint4 *>(rp + 16 * (4 * g + jp));
-            pk.sc = *reinterpret_cast<const uint2 *>(rp + kScaleOff + 8 * g);
-            pk.rope = *reinterpret_cast<const uint4 *>(rp + kRopeOff + 16 * g);
+        for (int jp = 0; jp < 8; ++jp) lat_off[jp] = 16 * (8 * g + (jp ^ fp8_swz(row)));
+        auto load_packed = [&](int T, Packed &pk) {
+            const uint8_t *rp = ring + (T % kNBuf) * kTileBytes + row * kRowB;
+            if constexpr (kFp8) {
+#pragma unroll
+                for (int jp = 0; jp < 8; ++jp) pk.lat[jp] = *reinterpret_cast<const uint4 *>(rp + lat_off[jp]);
+            } else {
+#pragma unroll
+                for (int jp = 0; jp < 4; ++jp)
+                    pk.nib[jp] = *reinterpret_cast<const uint4 *>(rp + 16 * (4 * g + jp));
+                pk.sc = *reinterpret_cast<const uint2 *>(rp + kScaleOff + 8 * g);
+            }
+            pk.rope = *reinterpret_cast<const uint4 *>(rp + R::kRopeAt + 16 * g);
         };
         // unpack and score: d = scale_log2 * q.k - m_run of this wave's 16
         // rows (-inf for rows past the end of the list); sp = the {S,S}
         // block-scale pairs
         auto score = [&](int T, const Packed &pk, float (&d)[MB][4], half2_t (&sp)[8]) {
-            {
-                const uint32_t d0 = __builtin_amdgcn_perm(0u, pk.sc.x, 0x01010000u);
-                const uint32_t d1 = __builtin_amdgcn_perm(0u, pk.sc.x, 0x03030202u);
-                const uint32_t d2 = __builtin_amdgcn_perm(0u, pk.sc.y, 0x01010000u);
-                const uint32_t d3 = __builtin_amdgcn_perm(0u, pk.sc.y, 0x03030202u);
-                sp[0] = fp8x2<false>(d0); sp[1] = fp8x2<true>(d0);
-                sp[2] = fp8x2<false>(d1); sp[3] = fp8x2<true>(d1);
-                sp[4] = fp8x2<false>(d2); sp[5] = fp8x2<true>(d2);
-                sp[6] = fp8x2<false>(d3); sp[7] = fp8x2<true>(d3);
-            }
             float4_t acc[MB];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+            if constexpr (kFp8) {
+                // E4M3 latent bytes -> f16, exact; dims 128g + 8j .. are bytes 8j ..
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const uint32_t w = pk.nib[j >> 2][j & 3];
-                const half2_t sv = sp[2 * (j >> 2) + ((j & 3) >> 1)];
-                const half8_t kb = join(fp4x2<0>(w) * sv, fp4x2<1>(w) * sv, fp4x2<2>(w) * sv,
-                                        fp4x2<3>(w) * sv);
+                for (int j = 0; j < 16; ++j) {
+                    const uint32_t w0 = pk.lat[j >> 1][2 * (j & 1)], w1 = pk.lat[j >> 1][2 * (j & 1) + 1];
+                    const half8_t kb = join(fp8x2<false>(w0), fp8x2<true>(w0), fp8x2<false>(w1),
+                                            fp8x2<true>(w1));
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[mb][j], kb, acc[mb], 0, 0, 0);
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[mb][j], kb, acc[mb], 0, 0, 0);
+                }
+            } else {
+                {
+                    const uint32_t d0 = __builtin_amdgcn_perm(0u, pk.sc.x, 0x01010000u);
+                    const uint32_t d1 = __builtin_amdgcn_perm(0u, pk.sc.x, 0x03030202u);
+                    const uint32_t d2 = __builtin_amdgcn_perm(0u, pk.sc.y, 0x01010000u);
+                    const uint32_t d3 = __builtin_amdgcn_perm(0u, pk.sc.y, 0x03030202u);
+                    sp[0] = fp8x2<false>(d0); sp[1] = fp8x2<true>(d0);
+                    sp[2] = fp8x2<false>(d1); sp[3] = fp8x2<true>(d1);
+                    sp[4] = fp8x2<false>(d2); sp[5] = fp8x2<true>(d2);
+                    sp[6] = fp8x2<false>(d3); sp[7] = fp8x2<true>(d3);
+                }
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const uint32_t w = pk.nib[j >> 2][j & 3];
+                    const half2_t sv = sp[2 * (j >> 2) + ((j & 3) >> 1)];
+                    const half8_t kb = join(fp4x2<0>(w) * sv, fp4x2<1>(w) * sv, fp4x2<2>(w) * sv,
+                                            fp4x2<3>(w) * sv);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[mb][j], kb, acc[mb], 0, 0, 0);
+                }
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -459,8 +528,10 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
             // the value waves, and the flag (any score past max + kSlack)
             const int pb = s & 1;
             write_weights(pb, d);
+            if constexpr (!kFp8) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) st_lds[pb][(8 * g + k) * kSStride + row] = sp[k][0];
+                for (int k = 0; k < 8; ++k) st_lds[pb][(8 * g + k) * kSStride + row] = sp[k][0];
+            }
             bool over = false;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -578,8 +649,9 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     // step s contracts tile s - 2 from registers (while the score waves
     // score tile s), then reads the operands of tile s - 1
     half8_t pa[4];
-    int2_t vv[4][2];
-    half8_t sv[4][2][2];
+    int2_t vv[4][2];       // NVFP4: packed values per (cb, rb)
+    half8_t sv[4][2][2];   // NVFP4: their block scales per (cb, rb, t)
+    int2_t vv8[4][4];      // FP8: E4M3 values per (cb, rt)
 
     // operands of tile s - 1 (read during step s, see below): the packed
     // values through the transposing 4-bit read (lanes 16G..16G+15 read 8
@@ -591,21 +663,50 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     // 16 g2 + lane % 16 of the 32-row half, columns 128 sw + 16 (lane / 16 % 2)
     // ..), block scales (block 8 sw + n32 / 16, rows 16 g2 ..), weights
     // (head n32, rows 16 g2 ..); the rest of each address is a constant
-    const uint32_t v_lane = (uint32_t)((16 * g2 + (lane & 15)) * kRowBytes + 64 * sw + 8 * ((lane >> 4) & 1));
+    const uint32_t v_lane = (uint32_t)((16 * g2 + (lane & 15)) * kRowB + 64 * sw + 8 * ((lane >> 4) & 1));
     const uint32_t s_lane = (uint32_t)(((8 * sw + (n32 >> 4)) * kSStride + 16 * g2) * 2);
     const uint32_t p_lane = (uint32_t)((n32 * kPStride + 16 * g2) * 2);
+    // FP8: the transposing 8-bit read gives lane 8h + p of a 16-lane group
+    // byte p of the 8-byte words of lanes h, h+2, .., h+14 of the group
+    // (probed on the device).  So for MFMA (rb, t) lane l supplies row
+    // 32 rb + 8 t + 16 (l/32) + (l%16)/2, column window 128 sw + 32 cb +
+    // 16 ((l/16)%2) + 8 (l%2), and receives column 128 sw + 32 cb + n32 of
+    // rows 32 rb + 16 g2 + 8 t .. + 7: its B operand, in the row order of
+    // the weights.  The window's piece is permuted by fp8_swz of the row,
+    // which does not depend on (rb, t), so one lane offset per cb serves all
+    // four.
+    uint32_t v8_lane[4];
+    {
+        const int r = 16 * g2 + ((lane & 15) >> 1);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+            v8_lane[cb] = (uint32_t)(r * kRowB + 16 * ((8 * sw + 2 * cb + ((lane >> 4) & 1)) ^ fp8_swz(r)) +
+                                     8 * (lane & 1));
+    }
     auto read_values = [&](int s, int rb) {
         const int pb = (s + 1) & 1;  // parity of tile s - 1
-        const uint8_t *vb = ring + ((s + kNBuf - 1) % kNBuf) * kTileBytes + v_lane;
-        const uint8_t *sb = reinterpret_cast<const uint8_t *>(st_lds[pb]) + s_lane;
+        const uint8_t *tb = ring + ((s + kNBuf - 1) % kNBuf) * kTileBytes;
+        if constexpr (kFp8) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            // columns 128 sw + 32 cb + n32: packed bytes 16 cb further, block 2 cb further
-            vv[cb][rb] = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_int2_t *)(
-                (__attribute__((address_space(3))) const uint8_t *)(vb + 32 * rb * kRowBytes + 16 * cb)));
-            const half8_t *sp8 = reinterpret_cast<const half8_t *>(sb + (2 * cb * kSStride + 32 * rb) * 2);
-            sv[cb][rb][0] = sp8[0];
-            sv[cb][rb][1] = sp8[1];
+            for (int cb = 0; cb < 4; ++cb) {
+                const uint8_t *vb = tb + v8_lane[cb];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    vv8[cb][2 * rb + t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_int2_t *)(
+                        (__attribute__((address_space(3))) const uint8_t *)(vb + (32 * rb + 8 * t) * kRowB)));
+            }
+        } else {
+            const uint8_t *vb = tb + v_lane;
+            const uint8_t *sb = reinterpret_cast<const uint8_t *>(st_lds[pb]) + s_lane;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                // columns 128 sw + 32 cb + n32: packed bytes 16 cb further, block 2 cb further
+                vv[cb][rb] = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_int2_t *)(
+                    (__attribute__((address_space(3))) const uint8_t *)(vb + 32 * rb * kRowB + 16 * cb)));
+                const half8_t *sp8 = reinterpret_cast<const half8_t *>(sb + (2 * cb * kSStride + 32 * rb) * 2);
+                sv[cb][rb][0] = sp8[0];
+                sv[cb][rb][1] = sp8[1];
+            }
         }
     };
 
@@ -617,14 +718,14 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     for (int T = 0; T <= 1 && T < n_tiles; ++T) issue(T);
     if (n_tiles > 0) wait_tile(min(1, n_tiles - 1));
     __syncthreads();
-    if (2 < n_tiles) issue(2);
-    uint32_t r6[6];  // row ids of the next tile to load
-    if (3 < n_tiles) tile_rows(3, r6);
+    for (int T = 2; T < kAhead && T < n_tiles; ++T) issue(T);
+    uint32_t rk[kMaxDma];  // row ids of the next tile to load
+    if (kAhead < n_tiles) tile_rows(kAhead, rk);
 
     for (int s = 0; s <= n_tiles + 1; ++s) {
         // tile s + 1 complete before B(s): at most the tiles issued after it
-        // (s + 2 .. min(s + kNBuf - 3, n_tiles - 1)) may be outstanding
-        if (s >= 1 && s + 1 < n_tiles) wait_tile(min(kNBuf - 4, n_tiles - 2 - s));
+        // (s + 2 .. min(s + kAhead - 1, n_tiles - 1)) may be outstanding
+        if (s >= 1 && s + 1 < n_tiles) wait_tile(min(kAhead - 2, n_tiles - 2 - s));
         __syncthreads();                                                // B(s)
         asm volatile("" : "+v"(ones));  // kept in registers, not rebuilt per use
         // step s contracts tile s - 2 (operands in registers) and reads the
@@ -635,14 +736,13 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         if (cur) fl = read_flags((s - 1) & 1);
         if (s == 0) {
             // tile 1 (read by the score waves after F0) is complete before F0
-            if (1 < n_tiles) wait_tile(2 < n_tiles ? 1 : 0);
+            if (1 < n_tiles) wait_tile(min(kAhead - 2, n_tiles - 2));
             __syncthreads();                                            // F0
         }
-        // tile s + 3 into the slot of tile s - 2 (read for the last time in
-        // step s - 1), as early as possible; its row ids were read in step
+        // tile s + kAhead into the slot of tile s - 2 (read for the last time
+        // in step s - 1), as early as possible; its row ids were read in step
         // s - 1
-        const bool more = s + kNBuf - 2 < n_tiles;
-        if (more) tile_dma(s + kNBuf - 2, r6);
+        if (s + kAhead < n_tiles) tile_dma(s + kAhead, rk);
         // the weights of tile s - 1 (A operands); read again after S(s)
         // when the score waves re-weight that tile
         const int pb = (s - 1) & 1;
@@ -661,12 +761,17 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                 const int rb = rt >> 1, t = rt & 1;
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb) {
-                    const uint32_t w = (uint32_t)vv[cb][rb][t];
-                    const half8_t ss = sv[cb][rb][t];
-                    const half2_t s01 = {ss[0], ss[1]}, s23 = {ss[2], ss[3]}, s45 = {ss[4], ss[5]},
-                                  s67 = {ss[6], ss[7]};
-                    const half8_t vb = join(fp4x2<0>(w) * s01, fp4x2<1>(w) * s23, fp4x2<2>(w) * s45,
-                                            fp4x2<3>(w) * s67);
+                    half8_t vb;
+                    if constexpr (kFp8) {
+                        const uint32_t w0 = (uint32_t)vv8[cb][rt][0], w1 = (uint32_t)vv8[cb][rt][1];
+                        vb = join(fp8x2<false>(w0), fp8x2<true>(w0), fp8x2<false>(w1), fp8x2<true>(w1));
+                    } else {
+                        const uint32_t w = (uint32_t)vv[cb][rb][t];
+                        const half8_t ss = sv[cb][rb][t];
+                        const half2_t s01 = {ss[0], ss[1]}, s23 = {ss[2], ss[3]}, s45 = {ss[4], ss[5]},
+                                      s67 = {ss[6], ss[7]};
+                        vb = join(fp4x2<0>(w) * s01, fp4x2<1>(w) * s23, fp4x2<2>(w) * s45, fp4x2<3>(w) * s67);
+                    }
                     o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[rt], vb, o[cb], 0, 0, 0);
                 }
                 if (rt == sw) lacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[rt], ones, lacc, 0, 0, 0);
@@ -679,7 +784,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) read_weights(rt);
         }
-        if (s + kNBuf - 1 < n_tiles) tile_rows(s + kNBuf - 1, r6);
+        if (s + kAhead + 1 < n_tiles) tile_rows(s + kAhead + 1, rk);
         if (cur && flag_mask(fl) != 0) {
             // tile s - 1 moved the running max: the score waves re-weight
             // it before S(s); O and the sum (tiles up to s - 2) are rescaled
@@ -812,7 +917,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(
 
 }  // namespace
 
-DecodePlan plan_decode(int batch, int heads, int topk) {
+DecodePlan plan_decode(int batch, int heads, int topk, RowFormat fmt) {
     DecodePlan p;
     p.heads_per_group = heads >= 32 ? 32 : 16;
     p.groups = heads / p.heads_per_group;
@@ -823,6 +928,10 @@ DecodePlan plan_decode(int batch, int heads, int topk) {
     s = s < 1 ? 1 : s;
     s = s > max_s ? max_s : s;
     s = s > kMaxSplits ? kMaxSplits : s;
+    // a split scans at most the row ids its LDS holds
+    const int max_per = fmt == kFmtFp8 ? Ring<kFmtFp8>::kMaxPerSplit : Ring<kFmtNvfp4>::kMaxPerSplit;
+    const int min_s = (topk + max_per - 1) / max_per;
+    s = s < min_s ? min_s : s;
     p.splits = s;
     p.per_split = (topk + s - 1) / s;
     p.partial_bytes = (size_t)p.heads_per_group * kLatent * sizeof(_Float16) +
@@ -842,7 +951,7 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
                                     const int32_t *seq_lens, const int32_t *topk_idx,
                                     int32_t batch, int32_t heads, int32_t topk, float scale,
                                     float *out, float *lse, void *workspace,
-                                    const DecodePlan &plan, hipStream_t stream) {
+                                    const DecodePlan &plan, RowFormat fmt, hipStream_t stream) {
     const int blocks = ((batch + 7) / 8) * 8 * plan.groups * plan.splits;
     const int units = batch * plan.groups;
     _Float16 *part_o = nullptr;
@@ -855,16 +964,19 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
                                             ((o_bytes + 255) & ~(size_t)255));
     }
     const float scale_log2 = (float)((double)scale * 1.4426950408889634074);
-    if (plan.heads_per_group == 32)
-        hipLaunchKernelGGL(sparse_mla_decode_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream,
-                           q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,
-                           topk, scale_log2, out, lse, part_o, part_ml, batch, plan.groups,
-                           plan.splits, plan.per_split);
-    else
-        hipLaunchKernelGGL(sparse_mla_decode_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream,
-                           q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,
-                           topk, scale_log2, out, lse, part_o, part_ml, batch, plan.groups,
-                           plan.splits, plan.per_split);
+#define SMLA_LAUNCH(MB, FMT)                                                                 \
+    hipLaunchKernelGGL((sparse_mla_decode_kernel<MB, FMT>), dim3(blocks), dim3(kThreads), 0, stream, \
+                       q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,      \
+                       topk, scale_log2, out, lse, part_o, part_ml, batch, plan.groups,            \
+                       plan.splits, plan.per_split)
+    if (fmt == kFmtFp8) {
+        if (plan.heads_per_group == 32) SMLA_LAUNCH(2, kFmtFp8);
+        else SMLA_LAUNCH(1, kFmtFp8);
+    } else {
+        if (plan.heads_per_group == 32) SMLA_LAUNCH(2, kFmtNvfp4);
+        else SMLA_LAUNCH(1, kFmtNvfp4);
+    }
+#undef SMLA_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
     // one wave per (unit, head); the blocks of XCD x take the sequences b = x mod 8

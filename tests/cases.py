@@ -85,29 +85,39 @@ def small_case(batch, heads, lens, topk, seed=0, pages="global", pad=None, dup=0
                 scale=1.0 / np.sqrt(576.0))
 
 
-def oracle_cache(case) -> np.ndarray:
-    cache = np.zeros((case["num_pages"], 64, 352), dtype=np.uint8)
+ROW_BYTES = {"nvfp4": oracle.ROW_BYTES, "fp8": oracle.FP8_ROW_BYTES}
+
+
+def oracle_cache(case, fmt: str = "nvfp4") -> np.ndarray:
+    """The case's rows appended by the oracle into a cache of the given row format."""
+    cache = np.zeros((case["num_pages"], 64, ROW_BYTES[fmt]), dtype=np.uint8)
+    append = oracle.kv_quant_append if fmt == "nvfp4" else oracle.kv_quant_append_fp8
     for b, bits in enumerate(case["rows"]):
         if bits.shape[0]:
-            oracle.kv_quant_append(bits, wl.slots_for(case["pt"], b, 0, bits.shape[0]), cache)
+            append(bits, wl.slots_for(case["pt"], b, 0, bits.shape[0]), cache)
     return cache
 
 
-def gpu_cache(case, dev, smla) -> torch.Tensor:
-    cache = torch.zeros((case["num_pages"], 64, 352), dtype=torch.uint8, device=dev)
+def gpu_cache(case, dev, smla, fmt: str = "nvfp4") -> torch.Tensor:
+    """The case's rows appended by the library into a device cache."""
+    cache = torch.zeros((case["num_pages"], 64, ROW_BYTES[fmt]), dtype=torch.uint8, device=dev)
+    append = smla.kv_quant_append if fmt == "nvfp4" else smla.kv_quant_append_fp8
     for b, bits in enumerate(case["rows"]):
         if bits.shape[0]:
             slots = torch.as_tensor(wl.slots_for(case["pt"], b, 0, bits.shape[0]), device=dev)
-            smla.kv_quant_append(to_dev_bf16(bits, dev), slots, cache)
+            append(to_dev_bf16(bits, dev), slots, cache)
     return cache
 
 
 def gpu_decode(case, cache_dev, dev, smla):
+    """Decode through the library; the cache's row size picks the entry point."""
     q = to_dev_bf16(case["q"], dev)
     pt = torch.as_tensor(np.ascontiguousarray(case["pt"]), device=dev)
     sl = torch.as_tensor(np.ascontiguousarray(case["lens"].astype(np.int32)), device=dev)
     tk = torch.as_tensor(np.ascontiguousarray(case["topk"]), device=dev)
-    out, lse = smla.sparse_mla_decode(q, cache_dev, pt, sl, tk, case["scale"])
+    fn = smla.sparse_mla_decode if cache_dev.shape[2] == oracle.ROW_BYTES \
+        else smla.sparse_mla_decode_fp8
+    out, lse = fn(q, cache_dev, pt, sl, tk, case["scale"])
     torch.cuda.synchronize(dev)
     return out.cpu().numpy(), lse.cpu().numpy()
 

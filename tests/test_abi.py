@@ -49,65 +49,84 @@ def test_workspace_sizes():
     assert smla.decode_workspace_bytes(1, 16, 64) == 0
 
 
+def test_workspace_sizes_fp8():
+    import sparse_mla_decode_amd as smla
+    assert smla.decode_workspace_bytes_fp8(0, 64, 2048) == 0
+    assert smla.decode_workspace_bytes_fp8(4, 32, 2048) == 0
+    assert smla.decode_workspace_bytes_fp8(4, 64, 4096) == 0
+    # an FP8 workgroup covers at most 1024 list entries: a 2048-entry list is
+    # always split in two or more, so even a full batch needs partials
+    ws = smla.decode_workspace_bytes_fp8(128, 16, 2048)
+    assert ws >= 128 * 2 * (16 * 512 * 2 + 16 * 2 * 4)
+    assert ws % 256 == 0
+    assert smla.decode_workspace_bytes_fp8(1, 16, 1024) >= 0
+    assert smla.decode_workspace_bytes_fp8(1, 16, 64) == 0
+
+
 FAKE = 0x10000  # never dereferenced: every call below fails host-side validation
 
 
-def _decode(**kw):
+def _decode(fmt="", **kw):
     import sparse_mla_decode_amd as smla
     a = dict(q=FAKE, cache=FAKE, num_pages=10, page_table=FAKE, max_pages=4, seq_lens=FAKE,
              topk_indices=FAKE, batch=2, heads=16, topk=64, scale=0.04, out=FAKE, lse=FAKE,
              ws=FAKE, ws_bytes=1 << 30, stream=None)
     a.update(kw)
-    return smla.lib.smla_sparse_mla_decode(a["q"], a["cache"], a["num_pages"], a["page_table"],
-                                           a["max_pages"], a["seq_lens"], a["topk_indices"],
-                                           a["batch"], a["heads"], a["topk"], a["scale"],
-                                           a["out"], a["lse"], a["ws"], a["ws_bytes"],
-                                           a["stream"])
+    fn = getattr(smla.lib, "smla_sparse_mla_decode" + fmt)
+    return fn(a["q"], a["cache"], a["num_pages"], a["page_table"], a["max_pages"], a["seq_lens"],
+              a["topk_indices"], a["batch"], a["heads"], a["topk"], a["scale"], a["out"],
+              a["lse"], a["ws"], a["ws_bytes"], a["stream"])
 
 
-def test_decode_rejects_bad_arguments():
-    assert _decode(heads=32) == -3
-    assert _decode(heads=8) == -3
-    assert _decode(topk=0) == -2
-    assert _decode(topk=2049) == -2
-    assert _decode(batch=0) == -2
-    assert _decode(max_pages=0) == -2
-    assert _decode(num_pages=0) == -2
-    assert _decode(num_pages=(1 << 25) + 1) == -2
-    assert _decode(q=None) == -1
-    assert _decode(cache=None) == -1
-    assert _decode(lse=None) == -1
-    assert _decode(q=FAKE + 2) == -4
-    assert _decode(out=FAKE + 4) == -4
-    assert _decode(cache=FAKE + 16) == -4
-    assert _decode(topk_indices=FAKE + 1) == -4
+@pytest.mark.parametrize("fmt", ["", "_fp8"])
+def test_decode_rejects_bad_arguments(fmt):
+    def d(**kw):
+        return _decode(fmt, **kw)
+    assert d(heads=32) == -3
+    assert d(heads=8) == -3
+    assert d(topk=0) == -2
+    assert d(topk=2049) == -2
+    assert d(batch=0) == -2
+    assert d(max_pages=0) == -2
+    assert d(num_pages=0) == -2
+    assert d(num_pages=(1 << 25) + 1) == -2
+    assert d(q=None) == -1
+    assert d(cache=None) == -1
+    assert d(lse=None) == -1
+    assert d(q=FAKE + 2) == -4
+    assert d(out=FAKE + 4) == -4
+    assert d(cache=FAKE + 16) == -4
+    assert d(topk_indices=FAKE + 1) == -4
     # batch 1 x 64 heads needs split partials: missing or short workspace
-    assert _decode(batch=1, heads=64, topk=2048, ws=None, ws_bytes=0) == -5
-    assert _decode(batch=1, heads=64, topk=2048, ws_bytes=1024) == -5
-    assert _decode(batch=1, heads=64, topk=2048, ws=FAKE + 64) == -4
+    assert d(batch=1, heads=64, topk=2048, ws=None, ws_bytes=0) == -5
+    assert d(batch=1, heads=64, topk=2048, ws_bytes=1024) == -5
+    assert d(batch=1, heads=64, topk=2048, ws=FAKE + 64) == -4
     # valid arguments on a machine without a gfx950 device: refused, nothing launched
     import torch
     if not torch.cuda.is_available():
-        assert _decode() == -7
+        assert d() == -7
 
 
-def _append(**kw):
+def _append(fmt="", **kw):
     import sparse_mla_decode_amd as smla
     a = dict(rows=FAKE, n=5, slots=FAKE, cache=FAKE, num_pages=3, stream=None)
     a.update(kw)
-    return smla.lib.smla_kv_quant_append(a["rows"], a["n"], a["slots"], a["cache"],
-                                         a["num_pages"], a["stream"])
+    fn = getattr(smla.lib, "smla_kv_quant_append" + fmt)
+    return fn(a["rows"], a["n"], a["slots"], a["cache"], a["num_pages"], a["stream"])
 
 
-def test_append_rejects_bad_arguments():
-    assert _append(n=-1) == -2
-    assert _append(num_pages=0) == -2
-    assert _append(rows=None) == -1
-    assert _append(slots=None) == -1
-    assert _append(rows=FAKE + 8) == -4
-    assert _append(cache=FAKE + 128) == -4
-    assert _append(slots=FAKE + 2) == -4
-    assert _append(n=0, rows=None) == 0          # nothing to do, nothing touched
+@pytest.mark.parametrize("fmt", ["", "_fp8"])
+def test_append_rejects_bad_arguments(fmt):
+    def ap(**kw):
+        return _append(fmt, **kw)
+    assert ap(n=-1) == -2
+    assert ap(num_pages=0) == -2
+    assert ap(rows=None) == -1
+    assert ap(slots=None) == -1
+    assert ap(rows=FAKE + 8) == -4
+    assert ap(cache=FAKE + 128) == -4
+    assert ap(slots=FAKE + 2) == -4
+    assert ap(n=0, rows=None) == 0          # nothing to do, nothing touched
 
 
 def test_binding_refuses_cpu_tensors():
@@ -118,3 +137,5 @@ def test_binding_refuses_cpu_tensors():
     cache = torch.zeros((1, 64, 352), dtype=torch.uint8)
     with pytest.raises(ValueError):
         smla.kv_quant_append(rows, slots, cache)
+    with pytest.raises(ValueError):
+        smla.kv_quant_append_fp8(rows, slots, torch.zeros((1, 64, 576), dtype=torch.uint8))

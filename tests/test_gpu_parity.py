@@ -228,7 +228,9 @@ def _ascending_lists(case, cache_o, qmul):
     q = _bf16_to_f32(case["q"]) * np.float32(qmul)
     case = dict(case, q=wl.bf16_bits(torch.from_numpy(q).to(torch.bfloat16)))
     qf = _bf16_to_f32(case["q"]).astype(np.float64)
-    vals = oracle.dequant_rows(cache_o.reshape(-1, 352))
+    rb = cache_o.shape[2]
+    vals = (oracle.dequant_rows if rb == oracle.ROW_BYTES else oracle.dequant_rows_fp8)(
+        cache_o.reshape(-1, rb))
     tk = case["topk"].copy()
     B, H, K = qf.shape[0], qf.shape[1], tk.shape[1]
     scores = np.full((B, H, K), -np.inf)
@@ -304,13 +306,20 @@ def test_decode_running_max_moves(dev, smla, batch, heads):
 # full-size workloads: all queries on the GPU, sampled sequences on the oracle
 # --------------------------------------------------------------------------
 
-def _full_workload_check(dev, smla, name, sample, seed=0):
+def _full_workload_check(dev, smla, name, sample, seed=0, fmt="nvfp4"):
     w = wl.WORKLOADS[name]
+    rb = oracle.ROW_BYTES if fmt == "nvfp4" else oracle.FP8_ROW_BYTES
+    quant = oracle.quant_rows if fmt == "nvfp4" else oracle.quant_rows_fp8
     lens = wl.context_lengths(w, seed)
     pt, num_pages = wl.build_page_table(w, lens, seed)
-    note("full %s: %d pages (%.2f GB)" % (name, num_pages, num_pages * 22528 / 1e9))
-    cache = torch.zeros((num_pages, 64, 352), dtype=torch.uint8, device=dev)
-    append = lambda rows, slots: smla.kv_quant_append(rows, slots, cache)
+    note("full %s %s: %d pages (%.2f GB)" % (name, fmt, num_pages, num_pages * 64 * rb / 1e9))
+    cache = torch.zeros((num_pages, 64, rb), dtype=torch.uint8, device=dev)
+    if fmt == "nvfp4":
+        append = lambda rows, slots: smla.kv_quant_append(rows, slots, cache)
+        decode = smla.sparse_mla_decode
+    else:
+        append = lambda rows, slots: smla.kv_quant_append_fp8(rows, slots, cache)
+        decode = smla.sparse_mla_decode_fp8
     wl.fill_cache(w, seed, lens, pt, append, dev, tail=w.append_tail)
     if w.append_tail:
         rows, slots = wl.tail_rows(w, seed, lens, pt, dev, w.append_tail)
@@ -319,27 +328,27 @@ def _full_workload_check(dev, smla, name, sample, seed=0):
     tk = wl.topk_indices(w, lens, seed)
     q = wl.queries(w, seed, device=dev)
     note("  decode")
-    out, lse = smla.sparse_mla_decode(q, cache, torch.as_tensor(pt, device=dev),
-                                      torch.as_tensor(lens.astype(np.int32), device=dev),
-                                      torch.as_tensor(tk, device=dev), w.softmax_scale)
+    out, lse = decode(q, cache, torch.as_tensor(pt, device=dev),
+                      torch.as_tensor(lens.astype(np.int32), device=dev),
+                      torch.as_tensor(tk, device=dev), w.softmax_scale)
     torch.cuda.synchronize(dev)
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     assert np.isfinite(out).all() and np.isfinite(lse).all()
     qbits = wl.bf16_bits(q)
-    flat = cache.view(-1, 352)
+    flat = cache.view(-1, rb)
     worst = 0.0
     for b in sample:
         sel = tk[b][tk[b] >= 0].astype(np.int64)
         rows = wl.rows_at(w, seed, b, sel, device=dev)
         rbits = wl.bf16_bits(rows)
-        mine = oracle.quant_rows(rbits)
+        mine = quant(rbits)
         slots = wl.slots_for(pt, b, 0, int(lens[b]))[sel].astype(np.int64)
         got_bytes = flat[torch.as_tensor(slots, device=dev)].cpu().numpy()
         assert np.array_equal(got_bytes, mine), "cache bytes differ for sequence %d" % b
         # the oracle on the selected rows alone, in list order
         n = sel.size
-        mini = np.zeros(((n + 63) // 64, 64, 352), dtype=np.uint8)
-        mini.reshape(-1, 352)[:n] = mine
+        mini = np.zeros(((n + 63) // 64, 64, rb), dtype=np.uint8)
+        mini.reshape(-1, rb)[:n] = mine
         ro, rl = oracle.sparse_mla_decode(qbits[b:b + 1], mini,
                                           np.arange((n + 63) // 64, dtype=np.int32)[None],
                                           np.array([n]), np.arange(n, dtype=np.int32)[None],
