@@ -92,13 +92,16 @@ def summarize_kernel_stats(d):
         name = r["Name"]
         if "smla" not in name:
             continue
-        # demangled (smla::(anonymous namespace)::k<2>(...)) or mangled
-        # (_ZN4smla12_GLOBAL__N_11kILi2EEEv...) names -> k or k<2>
-        m = re.search(r"(kv_quant_append_kernel|sparse_mla_decode_kernel|merge_splits_kernel)"
-                      r"(?:ILi(\d+)E|<(\d+)>)?", name)
+        # demangled (smla::(anonymous namespace)::k<2, 1>(...)) or mangled
+        # (_ZN4smla12_GLOBAL__N_11kILi2ELi1EEEv...) names -> k or k<2, 1>
+        m = re.search(r"(kv_quant_append(?:_fp8)?_kernel|sparse_mla_decode_kernel|"
+                      r"merge_splits_kernel)(I(?:Li-?\d+E)+E|<[^>]*>)?", name)
         if not m:
             continue
-        short = m.group(1) + ("<%s>" % (m.group(2) or m.group(3)) if (m.group(2) or m.group(3)) else "")
+        targs = m.group(2) or ""
+        if targs.startswith("I"):
+            targs = "<%s>" % ", ".join(re.findall(r"Li(-?\d+)E", targs))
+        short = m.group(1) + targs
         out.append("%-60s %8s %12.3f %12.3f %12.3f" % (
             short[:60], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3))

@@ -86,6 +86,8 @@ def _load():
     lib.oracle_kv_quant_append_fp8.restype = i64
     lib.oracle_sparse_mla_decode_fp8.argtypes = lib.oracle_sparse_mla_decode.argtypes
     lib.oracle_sparse_mla_decode_fp8.restype = None
+    lib.oracle_stage_rows_fp8.argtypes = [P, i64, P, i32, P, P, i32, i32, P, P]
+    lib.oracle_stage_rows_fp8.restype = None
     lib.oracle_fp8_row_bytes.restype = ctypes.c_int
     lib.oracle_row_bytes.restype = ctypes.c_int
     lib.oracle_page_rows.restype = ctypes.c_int
@@ -199,6 +201,36 @@ def kv_quant_append_fp8(rows_bf16_bits: np.ndarray, slot_mapping: np.ndarray,
     assert x.shape == (s.shape[0], DIM)
     return int(_load().oracle_kv_quant_append_fp8(_ptr(x), x.shape[0], _ptr(s), _ptr(cache),
                                                   cache.shape[0]))
+
+
+def stage_rows_fp8(cache: np.ndarray, page_table: np.ndarray, seq_lens: np.ndarray,
+                   topk: np.ndarray, staged: np.ndarray | None = None):
+    """The staged path's gather-unpack: returns (staged [B*kpad/64, 64, 576]
+    lean FP8 rows, staged_topk [B, K]); entry e of sequence b goes to row
+    b*kpad + e (kpad = K rounded up to 64), staged_topk = e or -1.  Rows of
+    unusable entries keep the contents of `staged` (zeros if not given)."""
+    c = _c(cache, np.uint8)
+    pt = _c(page_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    tk = _c(topk, np.int32)
+    assert c.ndim == 3 and c.shape[1:] == (PAGE_ROWS, ROW_BYTES)
+    B, K = tk.shape
+    kpad = -(-K // PAGE_ROWS) * PAGE_ROWS
+    if staged is None:
+        staged = np.zeros((B * kpad // PAGE_ROWS, PAGE_ROWS, FP8_ROW_BYTES), dtype=np.uint8)
+    assert staged.dtype == np.uint8 and staged.flags.c_contiguous
+    assert staged.shape == (B * kpad // PAGE_ROWS, PAGE_ROWS, FP8_ROW_BYTES)
+    st = np.zeros((B, K), dtype=np.int32)
+    _load().oracle_stage_rows_fp8(_ptr(c), c.shape[0], _ptr(pt), pt.shape[1], _ptr(sl), _ptr(tk),
+                                  B, K, _ptr(staged), _ptr(st))
+    return staged, st
+
+
+def staged_tables(batch: int, topk_len: int):
+    """Page table and seq_lens of the staged copy: page [b][p] = b*kpad/64 + p."""
+    pp = -(-topk_len // PAGE_ROWS)
+    pt = np.arange(batch * pp, dtype=np.int32).reshape(batch, pp)
+    return pt, np.full(batch, pp * PAGE_ROWS, dtype=np.int32)
 
 
 def sparse_mla_decode(q_bf16_bits: np.ndarray, cache: np.ndarray, page_table: np.ndarray,

@@ -43,7 +43,9 @@
  *   - the lean FP8 row the byte table of [P1] compares against is the 576
  *     values as OCP E4M3 bytes in dim order (latent then rope), no scale,
  *     each the E4M3 value nearest the input (ties to even, saturating at
- *     448, sign copied) -- the same rule as the NVFP4 row's rope bytes.
+ *     448, sign copied) -- the same rule as the NVFP4 row's rope bytes;
+ *   - the staged path's temporary FP8 copy is that lean FP8 row, made from
+ *     the decoded NVFP4 values by the same nearest-E4M3 rule.
  *
  * Inputs must be finite; behaviour on NaN/Inf inputs is not defined here.
  */
@@ -402,6 +404,45 @@ void oracle_sparse_mla_decode_fp8(const uint16_t *q, const uint8_t *cache, int64
     decode_rows(q, cache, FP8_ROW_BYTES, oracle_dequant_row_fp8, num_pages, page_table,
                 max_pages, seq_lens, topk, batch, heads, topk_len, softmax_scale, out, lse,
                 nthreads);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Staged path [P1 staged-vs-native figure and the paragraph before it; P3   */
+/* first implementation]                                                    */
+/* ---------------------------------------------------------------------- */
+
+/* The staged path's gather-unpack: every usable entry e of topk[b] (the
+ * rule of decode_rows) has its NVFP4 row decoded and each of the 576 values
+ * re-encoded as the E4M3 value nearest it (ties to even, saturating at 448):
+ * a lean FP8 row, written to row b * kpad + e of `staged` (kpad = topk_len
+ * rounded up to 64), and staged_topk[b][e] = e.  An unusable entry gets
+ * staged_topk[b][e] = -1 and its staged row is left as it was.  Attention
+ * over the copy is then the FP8 decode with page table [b][p] = b * kpad/64
+ * + p and seq_lens = kpad. */
+void oracle_stage_rows_fp8(const uint8_t *cache, int64_t num_pages, const int32_t *page_table,
+                           int32_t max_pages, const int32_t *seq_lens, const int32_t *topk,
+                           int32_t batch, int32_t topk_len, uint8_t *staged, int32_t *staged_topk)
+{
+    int64_t kpad = ((int64_t)topk_len + PAGE_ROWS - 1) / PAGE_ROWS * PAGE_ROWS;
+    double k[DIM];
+    for (int32_t b = 0; b < batch; ++b) {
+        int64_t L = seq_lens[b];
+        for (int32_t e = 0; e < topk_len; ++e) {
+            int64_t t = topk[(int64_t)b * topk_len + e];
+            int32_t *st = staged_topk + (int64_t)b * topk_len + e;
+            *st = -1;
+            if (t < 0 || t >= L || (t / PAGE_ROWS) >= max_pages)
+                continue;
+            int64_t page = page_table[(int64_t)b * max_pages + t / PAGE_ROWS];
+            if (page < 0 || page >= num_pages)
+                continue;
+            oracle_dequant_row(cache + (page * PAGE_ROWS + t % PAGE_ROWS) * ROW_BYTES, k);
+            uint8_t *dst = staged + ((int64_t)b * kpad + e) * FP8_ROW_BYTES;
+            for (int d = 0; d < DIM; ++d)
+                dst[d] = oracle_e4m3_nearest(k[d], 1.0);
+            *st = e;
+        }
+    }
 }
 
 int oracle_row_bytes(void) { return ROW_BYTES; }
