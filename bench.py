@@ -9,7 +9,9 @@ Infinity Cache.
 
 Prints ONE JSON line (metric, value = effective KV GB/s over the step, ...,
 roofline of the decode kernel, cpu_baseline of the oracle on host cores).
-`--format fp8` runs the same step over the lean FP8 cache (576-byte rows).
+`--format fp8` runs the same step over the lean FP8 cache (576-byte rows);
+`--path staged` replaces the fused decode by the staged path (gather-unpack
+of the NVFP4 rows into a lean FP8 copy in HBM, then the FP8 decode over it).
 """
 from __future__ import annotations
 
@@ -94,7 +96,7 @@ def summarize_kernel_stats(d):
             continue
         # demangled (smla::(anonymous namespace)::k<2, 1>(...)) or mangled
         # (_ZN4smla12_GLOBAL__N_11kILi2ELi1EEEv...) names -> k or k<2, 1>
-        m = re.search(r"(kv_quant_append(?:_fp8)?_kernel|sparse_mla_decode_kernel|"
+        m = re.search(r"(kv_quant_append(?:_fp8)?_kernel|sparse_mla_decode_kernel|stage_rows_fp8_kernel|"
                       r"merge_splits_kernel)(I(?:Li-?\d+E)+E|<[^>]*>)?", name)
         if not m:
             continue
@@ -185,6 +187,8 @@ def main():
     ap.add_argument("--workload", default="allheads")
     ap.add_argument("--format", choices=("nvfp4", "fp8"), default="nvfp4",
                     help="cache row format: NVFP4 (352 B) or lean FP8 (576 B)")
+    ap.add_argument("--path", choices=("fused", "staged"), default="fused",
+                    help="decode path: the fused kernel, or the staged ablation (NVFP4 only)")
     ap.add_argument("--sets", type=int, default=0, help="rotating (q, top-k) sets (0 = auto)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -218,6 +222,8 @@ def main():
     torch.cuda.set_device(dev)
     w = wl.WORKLOADS[args.workload]
     fmt = args.format
+    if args.path == "staged" and fmt != "nvfp4":
+        raise SystemExit("--path staged reads an NVFP4 cache")
     rbytes = ROW_BYTES[fmt]
     append_bytes_per_row = 576 * 2 + rbytes      # BF16 row read + cache row written
     seed = args.seed
@@ -263,6 +269,18 @@ def main():
     ws_bytes = ws_fn(w.batch, w.heads, w.topk)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     log("%d rotating sets, %.1f MB of selected rows each" % (sets, per_call_bytes / 1e6))
+    if args.path == "staged":
+        pp = (w.topk + 63) // 64
+        staged = torch.empty((w.batch * pp, 64, 576), dtype=torch.uint8, device=dev)
+        staged_topk = torch.empty((w.batch, w.topk), dtype=torch.int32, device=dev)
+        spt, ssl = smla.staged_tables(w.batch, w.topk, dev)
+        ws_bytes = smla.decode_workspace_bytes_fp8(w.batch, w.heads, w.topk)
+        ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+        def decode_fn(q_, cache_, pt_, sl_, tk_, scale_, out, lse, workspace):
+            smla.stage_rows_fp8(cache_, pt_, sl_, tk_, staged=staged, staged_topk=staged_topk)
+            smla.sparse_mla_decode_fp8(q_, staged, spt, ssl, staged_topk, scale_, out=out,
+                                       lse=lse, workspace=workspace)
 
     def step(i, ev=None):
         s = i % sets
@@ -301,7 +319,7 @@ def main():
     dec_tflops = dec_flops / dec_s / 1e12
     ai = w.heads * FLOPS_PER_HEAD_ROW / rbytes
     ridge = MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    traffic = measured_traffic(traffic_key(w.name, fmt))
+    traffic = measured_traffic(traffic_key(w.name, fmt) + ("-staged" if args.path == "staged" else ""))
     if ai >= ridge:
         roof = {"bound": "mfma", "achieved": round(dec_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(dec_tflops / MFMA_F16_PEAK_TFLOPS, 4),
@@ -314,6 +332,7 @@ def main():
         "metric": ("sparse NVFP4-MLA decode: effective KV GB/s (% HBM peak) and queries/sec"
                    if fmt == "nvfp4" else
                    "sparse MLA decode over lean FP8 rows: effective KV GB/s and queries/sec"),
+        "path": args.path,
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,

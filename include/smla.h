@@ -181,6 +181,43 @@ int smla_sparse_mla_decode_fp8(const void *q_bf16, const uint8_t *cache, int64_t
                                float *out, float *lse, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/*
+ * ---- Staged path (ablation of the fused decode) [P1 section "A kernel
+ * that reads four bits directly", the staged-vs-native figure and the
+ * paragraph before it; P3, the first implementation] ----
+ *
+ * smla_stage_rows_fp8 is the staged path's gather-unpack: it reads the
+ * selected NVFP4 rows and writes a lean FP8 copy of each to HBM, where
+ * smla_sparse_mla_decode_fp8 then reads it.  The two calls together move
+ * 352 + 576 + 576 bytes per selected row, against 352 for the fused
+ * smla_sparse_mla_decode; they exist to measure that difference.
+ *
+ *   cache .. topk       as for smla_sparse_mla_decode (an NVFP4 cache);
+ *                       entry usability follows the same rule
+ *   staged              [batch * kpad / 64][64][576] uint8, device, 256-B
+ *                       aligned, kpad = topk rounded up to a multiple of 64.
+ *                       Usable entry e of sequence b is written to row
+ *                       b * kpad + e: each of its 576 decoded values as the
+ *                       E4M3 byte nearest it (ties to even, saturating at
+ *                       +-448; the rope bytes are copied).  Rows of unusable
+ *                       entries are not written.
+ *   staged_topk         [batch][topk] int32, device: e for a usable entry,
+ *                       -1 otherwise
+ *
+ * Attention over the copy is smla_sparse_mla_decode_fp8 with cache =
+ * staged (num_pages = batch * kpad / 64), page_table [batch][kpad / 64]
+ * holding b * kpad / 64 + p, seq_lens all kpad, and topk_indices =
+ * staged_topk.  Errors: SMLA_ERR_SHAPE (batch not in [1, 65535], topk not in
+ * [1, 2048], max_pages < 1, num_pages not in [1, 2^25]), SMLA_ERR_NULL,
+ * SMLA_ERR_ALIGN (cache or staged not 256-B aligned, an int32 array not 4-B
+ * aligned), SMLA_ERR_DEVICE, SMLA_ERR_LAUNCH.  Asynchronous on `stream`;
+ * nothing is allocated.
+ */
+int smla_stage_rows_fp8(const uint8_t *cache, int64_t num_pages, const int32_t *page_table,
+                        int32_t max_pages, const int32_t *seq_lens, const int32_t *topk_indices,
+                        int32_t batch, int32_t topk, uint8_t *staged, int32_t *staged_topk,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,9 @@ not been built, importing this package raises.
         -> (out [B,H,512] fp32, lse [B,H] fp32)
     kv_quant_append_fp8, sparse_mla_decode_fp8
         the same over the lean FP8 row: cache [P,64,576] uint8
+    stage_rows_fp8, sparse_mla_decode_staged
+        the staged path (NVFP4 rows -> FP8 copy in HBM -> FP8 decode), kept
+        to measure the fused kernel against
 """
 from __future__ import annotations
 
@@ -39,7 +42,8 @@ ERRORS = {
 # exported symbols, in the order include/smla.h declares them
 EXPORTS = ("smla_strerror", "smla_version", "smla_kv_quant_append",
            "smla_decode_workspace_bytes", "smla_sparse_mla_decode", "smla_kv_quant_append_fp8",
-           "smla_decode_workspace_bytes_fp8", "smla_sparse_mla_decode_fp8")
+           "smla_decode_workspace_bytes_fp8", "smla_sparse_mla_decode_fp8",
+           "smla_stage_rows_fp8")
 
 
 class SmlaError(RuntimeError):
@@ -72,6 +76,8 @@ def _load() -> ctypes.CDLL:
         fn = getattr(lib, "smla_sparse_mla_decode" + sfx)
         fn.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, f32, P, P, P, sz, P]
         fn.restype = ctypes.c_int
+    lib.smla_stage_rows_fp8.argtypes = [P, i64, P, i32, P, P, i32, i32, P, P, P]
+    lib.smla_stage_rows_fp8.restype = ctypes.c_int
     return lib
 
 
@@ -208,3 +214,72 @@ def sparse_mla_decode_fp8(q: torch.Tensor, cache: torch.Tensor, page_table: torc
     return _decode(q, cache, page_table, seq_lens, topk, softmax_scale, out, lse, workspace,
                    stream, FP8_ROW_BYTES, lib.smla_sparse_mla_decode_fp8,
                    lib.smla_decode_workspace_bytes_fp8)
+
+
+_staged_tables: dict = {}
+
+
+def staged_tables(batch: int, topk: int, device: torch.device):
+    """Page table [batch][kpad/64] (b*kpad/64 + p) and seq_lens (all kpad) of
+    the staged copy, cached per (device, batch, topk)."""
+    key = (device.index, batch, topk)
+    with _ws_lock:
+        t = _staged_tables.get(key)
+        if t is None:
+            pp = (topk + PAGE_ROWS - 1) // PAGE_ROWS
+            pt = torch.arange(batch * pp, dtype=torch.int32, device=device).view(batch, pp)
+            sl = torch.full((batch,), pp * PAGE_ROWS, dtype=torch.int32, device=device)
+            t = _staged_tables[key] = (pt, sl)
+        return t
+
+
+
+def stage_rows_fp8(cache: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                   topk: torch.Tensor, staged: torch.Tensor | None = None,
+                   staged_topk: torch.Tensor | None = None, stream=None):
+    """The staged path's gather-unpack: NVFP4 rows of the usable entries ->
+    lean FP8 copy [B*kpad/64, 64, 576] (entry e of sequence b at row b*kpad+e)
+    and staged_topk [B, K] (e or -1).  Returns (staged, staged_topk)."""
+    _req(cache, "cache", torch.uint8, 3)
+    dev = cache.device
+    _req(page_table, "page_table", torch.int32, 2, dev)
+    _req(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _req(topk, "topk", torch.int32, 2, dev)
+    if tuple(cache.shape[1:]) != (PAGE_ROWS, ROW_BYTES):
+        raise ValueError("cache must be [num_pages,64,352]")
+    B, K = topk.shape
+    if page_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("page_table and seq_lens need one row per sequence")
+    pp = (K + PAGE_ROWS - 1) // PAGE_ROWS
+    if staged is None:
+        staged = torch.empty((B * pp, PAGE_ROWS, FP8_ROW_BYTES), dtype=torch.uint8, device=dev)
+    else:
+        _req(staged, "staged", torch.uint8, 3, dev)
+        if tuple(staged.shape) != (B * pp, PAGE_ROWS, FP8_ROW_BYTES):
+            raise ValueError("staged must be [B*ceil(K/64),64,576]")
+    if staged_topk is None:
+        staged_topk = torch.empty((B, K), dtype=torch.int32, device=dev)
+    else:
+        _req(staged_topk, "staged_topk", torch.int32, 2, dev)
+        if tuple(staged_topk.shape) != (B, K):
+            raise ValueError("staged_topk must be [B,K]")
+    _check(lib.smla_stage_rows_fp8(cache.data_ptr(), cache.shape[0], page_table.data_ptr(),
+                                   page_table.shape[1], seq_lens.data_ptr(), topk.data_ptr(), B, K,
+                                   staged.data_ptr(), staged_topk.data_ptr(),
+                                   _stream_ptr(dev, stream)))
+    return staged, staged_topk
+
+
+def sparse_mla_decode_staged(q: torch.Tensor, cache: torch.Tensor, page_table: torch.Tensor,
+                             seq_lens: torch.Tensor, topk: torch.Tensor, softmax_scale: float,
+                             out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                             staged: torch.Tensor | None = None,
+                             staged_topk: torch.Tensor | None = None,
+                             workspace: torch.Tensor | None = None, stream=None):
+    """The staged path end to end: stage_rows_fp8, then sparse_mla_decode_fp8
+    over the copy.  Returns (out, lse)."""
+    staged, staged_topk = stage_rows_fp8(cache, page_table, seq_lens, topk, staged, staged_topk,
+                                         stream)
+    spt, ssl = staged_tables(topk.shape[0], topk.shape[1], cache.device)
+    return sparse_mla_decode_fp8(q, staged, spt, ssl, staged_topk, softmax_scale, out=out,
+                                 lse=lse, workspace=workspace, stream=stream)

@@ -145,4 +145,24 @@ int smla_sparse_mla_decode_fp8(const void *q_bf16, const uint8_t *cache, int64_t
                   smla::kFmtFp8);
 }
 
+int smla_stage_rows_fp8(const uint8_t *cache, int64_t num_pages, const int32_t *page_table,
+                        int32_t max_pages, const int32_t *seq_lens, const int32_t *topk_indices,
+                        int32_t batch, int32_t topk, uint8_t *staged, int32_t *staged_topk,
+                        void *stream) {
+    if (batch < 1 || batch > 65535 || topk < 1 || topk > SMLA_MAX_TOPK || max_pages < 1 ||
+        num_pages < 1 || num_pages > ((int64_t)1 << 25))
+        return SMLA_ERR_SHAPE;
+    if (!cache || !page_table || !seq_lens || !topk_indices || !staged || !staged_topk)
+        return SMLA_ERR_NULL;
+    if (!aligned(cache, 256) || !aligned(staged, 256) || !aligned(page_table, 4) ||
+        !aligned(seq_lens, 4) || !aligned(topk_indices, 4) || !aligned(staged_topk, 4))
+        return SMLA_ERR_ALIGN;
+    const int dev = device_ok();
+    if (dev != SMLA_OK) return dev;
+    const hipError_t e = smla::launch_stage_rows_fp8(cache, num_pages, page_table, max_pages,
+                                                     seq_lens, topk_indices, batch, topk, staged,
+                                                     staged_topk, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -44,6 +44,12 @@ hipError_t launch_kv_quant_append(const uint16_t *rows, int64_t n, const int32_t
 hipError_t launch_kv_quant_append_fp8(const uint16_t *rows, int64_t n, const int32_t *slots,
                                       uint8_t *cache, int64_t num_pages, hipStream_t stream);
 
+hipError_t launch_stage_rows_fp8(const uint8_t *cache, int64_t num_pages,
+                                 const int32_t *page_table, int32_t max_pages,
+                                 const int32_t *seq_lens, const int32_t *topk_idx, int32_t batch,
+                                 int32_t topk, uint8_t *staged, int32_t *staged_topk,
+                                 hipStream_t stream);
+
 hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int64_t num_pages,
                                     const int32_t *page_table, int32_t max_pages,
                                     const int32_t *seq_lens, const int32_t *topk_idx,

@@ -529,8 +529,11 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
             const int pb = s & 1;
             write_weights(pb, d);
             if constexpr (!kFp8) {
+                // zero scales for the last tile's padding rows (see the value waves)
+                const bool real = (s + 1) * kTile <= n_valid || s * kTile + row < n_valid;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) st_lds[pb][(8 * g + k) * kSStride + row] = sp[k][0];
+                for (int k = 0; k < 8; ++k)
+                    st_lds[pb][(8 * g + k) * kSStride + row] = real ? sp[k][0] : (_Float16)0.0f;
             }
             bool over = false;
 #pragma unroll
@@ -710,6 +713,28 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         }
     };
 
+    // The last tile's padding rows (row 0 of page 0) carry zero weight, but a
+    // zero weight times a NaN value is NaN, so their value operands are made
+    // zero and bytes of rows nobody selected cannot reach the output: NVFP4 --
+    // the score waves write zero block scales for them; FP8 -- the bytes are
+    // cleared here once read.  rem = real rows of the tile (1..63); operand
+    // byte i of (cb, rt) is row 32 (rt / 2) + 16 g2 + 8 (rt % 2) + i.
+    auto mask_padding = [&](int rem) {
+        if constexpr (kFp8) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int k = min(max(rem - (32 * (rt >> 1) + 16 * g2 + 8 * (rt & 1)), 0), 8);
+                const uint32_t m0 = k >= 4 ? 0xFFFFFFFFu : (1u << (8 * k)) - 1u;
+                const uint32_t m1 = k >= 8 ? 0xFFFFFFFFu : (k <= 4 ? 0u : (1u << (8 * (k - 4))) - 1u);
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    vv8[cb][rt][0] &= (int)m0;
+                    vv8[cb][rt][1] &= (int)m1;
+                }
+            }
+        }
+    };
+
     // tiles 0 and 1 first (tile 2 follows once tile 0 is in, so that tile 0
     // and the query are not queued behind it), then wait until tile 0 is in
     // LDS.
@@ -784,6 +809,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) read_weights(rt);
         }
+        if (kFp8 && s == n_tiles && (n_valid & (kTile - 1)) != 0) mask_padding(n_valid & (kTile - 1));
         if (s + kAhead + 1 < n_tiles) tile_rows(s + kAhead + 1, rk);
         if (cur && flag_mask(fl) != 0) {
             // tile s - 1 moved the running max: the score waves re-weight

@@ -129,6 +129,33 @@ def test_append_rejects_bad_arguments(fmt):
     assert ap(n=0, rows=None) == 0          # nothing to do, nothing touched
 
 
+def test_stage_rejects_bad_arguments():
+    import sparse_mla_decode_amd as smla
+
+    def st(**kw):
+        a = dict(cache=FAKE, num_pages=10, page_table=FAKE, max_pages=4, seq_lens=FAKE,
+                 topk_indices=FAKE, batch=2, topk=64, staged=FAKE, staged_topk=FAKE, stream=None)
+        a.update(kw)
+        return smla.lib.smla_stage_rows_fp8(a["cache"], a["num_pages"], a["page_table"],
+                                            a["max_pages"], a["seq_lens"], a["topk_indices"],
+                                            a["batch"], a["topk"], a["staged"], a["staged_topk"],
+                                            a["stream"])
+    assert st(batch=0) == -2
+    assert st(topk=0) == -2
+    assert st(topk=2049) == -2
+    assert st(max_pages=0) == -2
+    assert st(num_pages=0) == -2
+    assert st(staged=None) == -1
+    assert st(staged_topk=None) == -1
+    assert st(cache=None) == -1
+    assert st(staged=FAKE + 16) == -4
+    assert st(cache=FAKE + 64) == -4
+    assert st(staged_topk=FAKE + 2) == -4
+    import torch
+    if not torch.cuda.is_available():
+        assert st() == -7
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     import sparse_mla_decode_amd as smla

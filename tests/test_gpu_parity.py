@@ -379,3 +379,31 @@ def test_full_ragged(dev, smla):
 
 def test_full_million(dev, smla):
     _full_workload_check(dev, smla, "million", sample=[0, 7])
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_decode_ignores_unselected_nan_row(dev, smla, fmt):
+    """The last tile is padded with row 0 of page 0; when that row is not
+    selected its bytes (here all 0xFF: NaN scales, NaN E4M3 values) must not
+    reach the output."""
+    note("decode with a NaN row 0 of page 0 (%s)" % fmt)
+    case = small_case(3, 64, [700, 300, 150], 2048, seed=61)
+    rb = 352 if fmt == "nvfp4" else 576
+    for b in range(3):
+        L = int(case["lens"][b])
+        owner = [t for t in range(0, L, 64) if case["pt"][b][t // 64] == 0]
+        for t in owner:                                     # token on page 0, row 0
+            case["topk"][b][case["topk"][b] == t] = -1
+    assert all((case["topk"][b] >= 0).sum() % 64 for b in range(3))     # ragged last tiles
+    cache_o = oracle_cache(case, fmt)
+    cache_o[0, 0, :] = 0xFF
+    cache_d = gpu_cache(case, dev, smla, fmt)
+    cache_d[0, 0, :] = 0xFF
+    assert np.array_equal(cache_d.cpu().numpy(), cache_o)
+    out, lse = gpu_decode(case, cache_d, dev, smla)
+    ref_o, ref_l = oracle_decode(case, cache_o)
+    assert np.isfinite(ref_o).all()
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    e_out, e_lse = rel_l2(out, ref_o), lse_err(lse, ref_l)
+    note("  rel_l2 %.3e lse %.3e" % (e_out, e_lse))
+    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
