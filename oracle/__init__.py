@@ -88,6 +88,8 @@ def _load():
     lib.oracle_sparse_mla_decode_fp8.restype = None
     lib.oracle_stage_rows_fp8.argtypes = [P, i64, P, i32, P, P, i32, i32, P, P]
     lib.oracle_stage_rows_fp8.restype = None
+    lib.oracle_topk_select.argtypes = [P, i64, P, i32, i32, P]
+    lib.oracle_topk_select.restype = None
     lib.oracle_fp8_row_bytes.restype = ctypes.c_int
     lib.oracle_row_bytes.restype = ctypes.c_int
     lib.oracle_page_rows.restype = ctypes.c_int
@@ -231,6 +233,18 @@ def staged_tables(batch: int, topk_len: int):
     pp = -(-topk_len // PAGE_ROWS)
     pt = np.arange(batch * pp, dtype=np.int32).reshape(batch, pp)
     return pt, np.full(batch, pp * PAGE_ROWS, dtype=np.int32)
+
+
+def topk_select(scores: np.ndarray, seq_lens: np.ndarray, topk: int) -> np.ndarray:
+    """[B, ld] float32 scores -> [B, topk] int32: the positions of the
+    min(topk, L_b) largest scores of row b (L_b = seq_lens[b] clamped to
+    [0, ld]), best first, equal scores by lower position, then -1."""
+    x = _c(scores, np.float32)
+    sl = _c(seq_lens, np.int32)
+    assert x.ndim == 2 and sl.shape == (x.shape[0],)
+    out = np.zeros((x.shape[0], topk), dtype=np.int32)
+    _load().oracle_topk_select(_ptr(x), x.shape[1], _ptr(sl), x.shape[0], int(topk), _ptr(out))
+    return out
 
 
 def sparse_mla_decode(q_bf16_bits: np.ndarray, cache: np.ndarray, page_table: np.ndarray,

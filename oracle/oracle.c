@@ -445,6 +445,53 @@ void oracle_stage_rows_fp8(const uint8_t *cache, int64_t num_pages, const int32_
     }
 }
 
+/* ---------------------------------------------------------------------- */
+/* Top-k select of the indexer's scores [P1 section "Decode: TP4, and the    */
+/* copies it keeps": an indexer picks the top cached positions, at most      */
+/* 2,048 per query; the prefill-timing figure's "DSA indexer (logits,       */
+/* top-k)"]                                                                  */
+/* ---------------------------------------------------------------------- */
+
+typedef struct {
+    float score;
+    int32_t index;
+} scored_t;
+
+/* higher score first; equal scores by lower index */
+static int by_score_desc(const void *pa, const void *pb)
+{
+    const scored_t *a = (const scored_t *)pa, *b = (const scored_t *)pb;
+    if (a->score > b->score)
+        return -1;
+    if (a->score < b->score)
+        return 1;
+    return (a->index > b->index) - (a->index < b->index);
+}
+
+/* For each query b: the positions of the min(topk, L_b) largest of
+ * scores[b][0 .. L_b), best first (equal scores by lower position), then -1
+ * up to topk.  L_b = seq_lens[b] clamped to [0, ld].  Scores must be finite. */
+void oracle_topk_select(const float *scores, int64_t ld, const int32_t *seq_lens, int32_t batch,
+                        int32_t topk, int32_t *out)
+{
+    for (int32_t b = 0; b < batch; ++b) {
+        int64_t L = seq_lens[b];
+        if (L < 0)
+            L = 0;
+        if (L > ld)
+            L = ld;
+        scored_t *v = (scored_t *)malloc(sizeof(scored_t) * (size_t)(L > 0 ? L : 1));
+        for (int64_t i = 0; i < L; ++i) {
+            v[i].score = scores[(int64_t)b * ld + i];
+            v[i].index = (int32_t)i;
+        }
+        qsort(v, (size_t)L, sizeof(scored_t), by_score_desc);
+        for (int32_t e = 0; e < topk; ++e)
+            out[(int64_t)b * topk + e] = e < L ? v[e].index : -1;
+        free(v);
+    }
+}
+
 int oracle_row_bytes(void) { return ROW_BYTES; }
 int oracle_fp8_row_bytes(void) { return FP8_ROW_BYTES; }
 int oracle_page_rows(void) { return PAGE_ROWS; }

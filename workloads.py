@@ -26,6 +26,11 @@ Recipe (stated once here, repeated in the design notes):
   * Top-k lists: ``uniform`` = min(K, L) distinct positions uniform over
     [0, L); ``recent`` = K/2 distinct from the last 6000 positions and K/2
     from the rest.  Lists are shuffled (never sorted) and padded with -1 to K.
+  * Indexer scores (input of the top-k select): N(0,1) fp32 per position;
+    for ``recent`` workloads the last 6000 positions get +RECENT_SHIFT, which
+    puts about half of the top 2048 of a 140K context in that window (the
+    shape of the ``recent`` lists).  Rows are [B, ld] with ld = max L rounded
+    up to a multiple of 4; positions at or past L_b hold 0.
 """
 from __future__ import annotations
 
@@ -223,6 +228,25 @@ def queries(w: Workload, seed: int = 0, set_id: int = 0, device="cpu",
     g = _torch_gen(device, seed, 3, set_id)
     x = torch.randn((B, w.heads, DIM), generator=g, device=device, dtype=torch.float32)
     return x.to(torch.bfloat16)
+
+
+RECENT_SHIFT = 1.5
+
+
+def index_scores(w: Workload, lens: np.ndarray, seed: int = 0, set_id: int = 0,
+                 device="cpu") -> torch.Tensor:
+    """Synthetic indexer scores [B, ld] fp32 (see the recipe above)."""
+    ld = int(-(-int(max(int(lens.max()), 1)) // 4) * 4)
+    out = torch.zeros((w.batch, ld), dtype=torch.float32, device=device)
+    for b in range(w.batch):
+        L = int(lens[b])
+        if L == 0:
+            continue
+        g = _torch_gen(device, seed, 5, set_id, b)
+        out[b, :L] = torch.randn((L,), generator=g, device=device, dtype=torch.float32)
+        if w.index == "recent":
+            out[b, max(0, L - TAIL):L] += RECENT_SHIFT
+    return out
 
 
 def iter_fill(w: Workload, seed: int, lens: np.ndarray, page_table: np.ndarray,
