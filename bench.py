@@ -12,6 +12,8 @@ roofline of the decode kernel, cpu_baseline of the oracle on host cores).
 `--format fp8` runs the same step over the lean FP8 cache (576-byte rows);
 `--path staged` replaces the fused decode by the staged path (gather-unpack
 of the NVFP4 rows into a lean FP8 copy in HBM, then the FP8 decode over it).
+`--op select` times the top-k select over the workload's synthetic indexer
+scores instead (its own JSON line).
 """
 from __future__ import annotations
 
@@ -96,7 +98,8 @@ def summarize_kernel_stats(d):
             continue
         # demangled (smla::(anonymous namespace)::k<2, 1>(...)) or mangled
         # (_ZN4smla12_GLOBAL__N_11kILi2ELi1EEEv...) names -> k or k<2, 1>
-        m = re.search(r"(kv_quant_append(?:_fp8)?_kernel|sparse_mla_decode_kernel|stage_rows_fp8_kernel|"
+        m = re.search(r"(kv_quant_append(?:_fp8)?_kernel|sparse_mla_decode_kernel|"
+                      r"stage_rows_fp8_kernel|topk_hist_kernel|topk_gather_kernel|"
                       r"merge_splits_kernel)(I(?:Li-?\d+E)+E|<[^>]*>)?", name)
         if not m:
             continue
@@ -179,6 +182,64 @@ def cpu_baseline(w, seed, lens, tk_np, qbits, budget_s, dev, fmt):
                          t_used, done / t_used)}
 
 
+def bench_select(args, w, dev):
+    """Time the top-k select over R rotating sets of synthetic indexer scores."""
+    import torch
+    import sparse_mla_decode_amd as smla
+    import workloads as wl
+    lens = wl.context_lengths(w, args.seed)
+    sl = torch.as_tensor(lens.astype(np.int32), device=dev)
+    first = wl.index_scores(w, lens, args.seed, 0, device=dev)
+    set_bytes = first.numel() * 4
+    sets = args.sets or max(2, math.ceil(2 * CACHE_BYTES_MALL / set_bytes) + 1)
+    scores = [first] + [wl.index_scores(w, lens, args.seed, s, device=dev) for s in range(1, sets)]
+    out = torch.empty((w.batch, w.topk), dtype=torch.int32, device=dev)
+    ws = smla.topk_workspace(dev, w.batch)
+    log("select %s: %d x %d scores, %d rotating sets" % (w.name, w.batch, first.shape[1], sets))
+    for i in range(args.warmup):
+        smla.topk_select(scores[i % sets], sl, w.topk, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        smla.topk_select(scores[(args.warmup + i) % sets], sl, w.topk, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    # algorithmic bytes: every valid score read once, the lists written once
+    alg = float(np.minimum(lens, first.shape[1]).sum()) * 4 + w.batch * w.topk * 4
+    gbps = alg / (us * 1e-6) / 1e9
+    result = {
+        "metric": "top-k select of indexer scores: scores GB/s and queries/sec",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "topk": w.topk,
+                   "scores_per_query": int(first.shape[1]), "rotating_sets": sets},
+        "select_us": round(us, 2), "queries_per_s": round(w.batch / (us * 1e-6), 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+    }
+    if not args.no_cpu:
+        import oracle
+        x = first.cpu().numpy()
+        t = time.perf_counter()
+        n = 0
+        while n < w.batch and time.perf_counter() - t < args.cpu_budget:
+            oracle.topk_select(x[n:n + 1], lens[n:n + 1], w.topk)
+            n += 1
+        dt = time.perf_counter() - t
+        cbytes = float(np.minimum(lens[:n], x.shape[1]).sum()) * 4
+        result["cpu_baseline"] = {"value": round(cbytes / dt / 1e9, 4), "unit": "GB/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": "oracle select (qsort, one thread) of %d of %d "
+                                            "queries, %.1f s" % (n, w.batch, dt)}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +248,8 @@ def main():
     ap.add_argument("--workload", default="allheads")
     ap.add_argument("--format", choices=("nvfp4", "fp8"), default="nvfp4",
                     help="cache row format: NVFP4 (352 B) or lean FP8 (576 B)")
+    ap.add_argument("--op", choices=("decode", "select"), default="decode",
+                    help="the decode step (default) or the top-k select alone")
     ap.add_argument("--path", choices=("fused", "staged"), default="fused",
                     help="decode path: the fused kernel, or the staged ablation (NVFP4 only)")
     ap.add_argument("--sets", type=int, default=0, help="rotating (q, top-k) sets (0 = auto)")
@@ -221,6 +284,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = wl.WORKLOADS[args.workload]
+    if args.op == "select":
+        bench_select(args, w, dev)
+        return
     fmt = args.format
     if args.path == "staged" and fmt != "nvfp4":
         raise SystemExit("--path staged reads an NVFP4 cache")

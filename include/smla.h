@@ -218,6 +218,38 @@ int smla_stage_rows_fp8(const uint8_t *cache, int64_t num_pages, const int32_t *
                         int32_t batch, int32_t topk, uint8_t *staged, int32_t *staged_topk,
                         void *stream);
 
+/*
+ * ---- Top-k select [P1 section "Decode: TP4, and the copies it keeps": an
+ * indexer picks the top cached positions, at most 2,048 per query; the
+ * prefill-timing figure lists the indexer's logits and top-k as separate
+ * steps] ----
+ *
+ * The step upstream of the decode: for each query b, the positions of the
+ * min(topk, L_b) largest of scores[b][0 .. L_b), then -1 up to topk, as the
+ * decode's topk_indices.  L_b = seq_lens[b] clamped to [0, ld].  The order of
+ * the list, and which of several equal scores at the threshold are taken,
+ * are unspecified (the set of scores taken is always the top min(topk, L_b)).
+ * Scores must be finite; -0 counts as just below +0.
+ *
+ *   scores        [batch][ld] fp32, device, 16-B aligned, ld a multiple of 4
+ *   seq_lens      [batch] int32, device
+ *   topk_indices  [batch][topk] int32, device (output)
+ *   workspace     smla_topk_workspace_bytes(batch) bytes, 256-B aligned.  It
+ *                 must be zero-filled before its first use; every call that
+ *                 returns SMLA_OK leaves it ready for the next call with any
+ *                 shape.  Calls that share a workspace must not overlap.
+ *
+ * Errors: SMLA_ERR_SHAPE (batch not in [1, 65535], topk not in [1, 2048], ld
+ * not a multiple of 4 in [4, 2^30]), SMLA_ERR_NULL, SMLA_ERR_ALIGN,
+ * SMLA_ERR_WORKSPACE (missing or short), SMLA_ERR_DEVICE, SMLA_ERR_LAUNCH.
+ * Asynchronous on `stream`; four kernel launches; nothing is allocated.
+ */
+size_t smla_topk_workspace_bytes(int32_t batch);
+
+int smla_topk_select(const float *scores, int64_t ld, const int32_t *seq_lens, int32_t batch,
+                     int32_t topk, int32_t *topk_indices, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,8 @@ not been built, importing this package raises.
     stage_rows_fp8, sparse_mla_decode_staged
         the staged path (NVFP4 rows -> FP8 copy in HBM -> FP8 decode), kept
         to measure the fused kernel against
+    topk_select(scores, seq_lens, topk) -> topk [B,K] int32
+        the positions of each query's K largest scores (the decode's list)
 """
 from __future__ import annotations
 
@@ -43,7 +45,7 @@ ERRORS = {
 EXPORTS = ("smla_strerror", "smla_version", "smla_kv_quant_append",
            "smla_decode_workspace_bytes", "smla_sparse_mla_decode", "smla_kv_quant_append_fp8",
            "smla_decode_workspace_bytes_fp8", "smla_sparse_mla_decode_fp8",
-           "smla_stage_rows_fp8")
+           "smla_stage_rows_fp8", "smla_topk_workspace_bytes", "smla_topk_select")
 
 
 class SmlaError(RuntimeError):
@@ -78,6 +80,10 @@ def _load() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.smla_stage_rows_fp8.argtypes = [P, i64, P, i32, P, P, i32, i32, P, P, P]
     lib.smla_stage_rows_fp8.restype = ctypes.c_int
+    lib.smla_topk_workspace_bytes.argtypes = [i32]
+    lib.smla_topk_workspace_bytes.restype = sz
+    lib.smla_topk_select.argtypes = [P, i64, P, i32, i32, P, P, sz, P]
+    lib.smla_topk_select.restype = ctypes.c_int
     return lib
 
 
@@ -283,3 +289,46 @@ def sparse_mla_decode_staged(q: torch.Tensor, cache: torch.Tensor, page_table: t
     spt, ssl = staged_tables(topk.shape[0], topk.shape[1], cache.device)
     return sparse_mla_decode_fp8(q, staged, spt, ssl, staged_topk, softmax_scale, out=out,
                                  lse=lse, workspace=workspace, stream=stream)
+
+
+_topk_workspaces: dict = {}
+
+
+def topk_workspace(device: torch.device, batch: int, stream=None) -> torch.Tensor:
+    """A zero-filled top-k workspace for at least `batch` queries, cached per
+    (device, stream); the select leaves it ready for the next call."""
+    need = int(lib.smla_topk_workspace_bytes(batch))
+    key = (device.index, _stream_ptr(device, stream))
+    with _ws_lock:
+        ws = _topk_workspaces.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
+            _topk_workspaces[key] = ws
+        return ws
+
+
+def topk_select(scores: torch.Tensor, seq_lens: torch.Tensor, topk: int,
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """scores [B, ld] fp32 (ld a multiple of 4), seq_lens [B] int32 ->
+    [B, topk] int32: the positions of the min(topk, L_b) largest scores of
+    each row (unordered), then -1."""
+    _req(scores, "scores", torch.float32, 2)
+    dev = scores.device
+    _req(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, ld = scores.shape
+    if seq_lens.shape[0] != B:
+        raise ValueError("seq_lens needs one entry per row of scores")
+    if out is None:
+        out = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    else:
+        _req(out, "out", torch.int32, 2, dev)
+        if tuple(out.shape) != (B, topk):
+            raise ValueError("out must be [B, topk]")
+    if workspace is None:
+        workspace = topk_workspace(dev, B, stream)
+    _check(lib.smla_topk_select(scores.data_ptr(), ld, seq_lens.data_ptr(), B, int(topk),
+                                out.data_ptr(), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(),
+                                _stream_ptr(dev, stream)))
+    return out

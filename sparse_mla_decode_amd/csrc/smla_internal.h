@@ -50,6 +50,12 @@ hipError_t launch_stage_rows_fp8(const uint8_t *cache, int64_t num_pages,
                                  int32_t topk, uint8_t *staged, int32_t *staged_topk,
                                  hipStream_t stream);
 
+// top-k select: uint32 words of workspace per query, and the launches
+int64_t topk_workspace_stride();
+hipError_t launch_topk_select(const float *scores, int64_t ld, const int32_t *seq_lens,
+                              int32_t batch, int32_t topk, int32_t *out, uint32_t *ws,
+                              hipStream_t stream);
+
 hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int64_t num_pages,
                                     const int32_t *page_table, int32_t max_pages,
                                     const int32_t *seq_lens, const int32_t *topk_idx,

@@ -156,6 +156,35 @@ def test_stage_rejects_bad_arguments():
         assert st() == -7
 
 
+def test_topk_select_rejects_bad_arguments():
+    import sparse_mla_decode_amd as smla
+    assert smla.lib.smla_topk_workspace_bytes(0) == 0
+    ws1 = smla.lib.smla_topk_workspace_bytes(1)
+    assert ws1 >= 4 * (2048 + 2048 + 1024) and smla.lib.smla_topk_workspace_bytes(10) == 10 * ws1
+
+    def tk(**kw):
+        a = dict(scores=FAKE, ld=4096, seq_lens=FAKE, batch=2, topk=2048, out=FAKE, ws=FAKE,
+                 ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return smla.lib.smla_topk_select(a["scores"], a["ld"], a["seq_lens"], a["batch"],
+                                         a["topk"], a["out"], a["ws"], a["ws_bytes"], a["stream"])
+    assert tk(batch=0) == -2
+    assert tk(topk=0) == -2
+    assert tk(topk=2049) == -2
+    assert tk(ld=0) == -2
+    assert tk(ld=4098) == -2                  # not a multiple of 4
+    assert tk(scores=None) == -1
+    assert tk(out=None) == -1
+    assert tk(scores=FAKE + 4) == -4
+    assert tk(out=FAKE + 2) == -4
+    assert tk(ws=None) == -5
+    assert tk(ws_bytes=ws1) == -5             # two queries need twice that
+    assert tk(ws=FAKE + 128) == -4
+    import torch
+    if not torch.cuda.is_available():
+        assert tk() == -7
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     import sparse_mla_decode_amd as smla

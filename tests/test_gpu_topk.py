@@ -1,0 +1,145 @@
+"""GPU parity of the top-k select against the CPU oracle, through the C ABI.
+
+Several lists are correct when scores tie at the threshold, and the list's
+order is unspecified, so the check compares what is unique -- the multiset
+of selected scores (the top min(K, L) values) and the -1 padding -- and
+checks that the rest is valid: distinct positions inside [0, L).  Where no
+scores tie the selected positions must equal the oracle's as a set.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from cases import lse_err, note, rel_l2, to_dev_bf16
+from test_gpu_parity import LSE_TOL, OUT_TOL
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def smla():
+    import sparse_mla_decode_amd as m
+    return m
+
+
+def check_lists(got: np.ndarray, scores: np.ndarray, lens: np.ndarray, K: int, exact_sets: bool):
+    want = oracle.topk_select(scores, lens, K)
+    for b in range(got.shape[0]):
+        L = int(min(max(int(lens[b]), 0), scores.shape[1]))
+        n = min(K, L)
+        g, w = got[b], want[b]
+        assert (g[n:] == -1).all(), b
+        sel = g[:n]
+        assert len(np.unique(sel)) == n, b
+        assert ((sel >= 0) & (sel < L)).all(), b
+        assert np.array_equal(np.sort(scores[b, sel]), np.sort(scores[b, w[:n]])), b
+        if exact_sets:
+            assert np.array_equal(np.sort(sel), np.sort(w[:n])), b
+
+
+def run(smla, dev, scores: np.ndarray, lens: np.ndarray, K: int):
+    s = torch.as_tensor(scores, device=dev)
+    sl = torch.as_tensor(lens.astype(np.int32), device=dev)
+    out = smla.topk_select(s, sl, K)
+    torch.cuda.synchronize(dev)
+    return out.cpu().numpy()
+
+
+def test_select_random_rows_and_lengths(dev, smla):
+    note("topk random rows")
+    rng = np.random.default_rng(1)
+    ld = 20000
+    lens = np.array([20000, 2049, 2048, 2047, 1, 0, 4097, 19999, 13, 8192], dtype=np.int64)
+    x = rng.standard_normal((lens.size, ld)).astype(np.float32)
+    got = run(smla, dev, x, lens, 2048)
+    check_lists(got, x, lens, 2048, exact_sets=True)
+
+
+@pytest.mark.parametrize("K", [1, 17, 256, 2048])
+def test_select_ties_at_the_threshold(dev, smla, K):
+    note("topk ties K=%d" % K)
+    rng = np.random.default_rng(2 + K)
+    ld = 12000
+    lens = np.array([12000, 9000, 5000, 3000], dtype=np.int64)
+    x = rng.integers(-20, 21, size=(4, ld)).astype(np.float32)    # 41 distinct values
+    x[3] = 7.0                                                      # one row all equal
+    x[2, ::2] = -0.0
+    x[2, 1::2] = 0.0                                                # signed zeros
+    got = run(smla, dev, x, lens, K)
+    check_lists(got, x, lens, K, exact_sets=False)
+
+
+def test_select_extreme_values_and_signs(dev, smla):
+    note("topk extreme values")
+    rng = np.random.default_rng(3)
+    ld = 8192
+    x = (rng.standard_normal((3, ld)) * 1e30).astype(np.float32)
+    x[1] = -np.abs(rng.standard_normal(ld)).astype(np.float32)     # all negative
+    x[2] = rng.standard_normal(ld).astype(np.float32) * 1e-40      # subnormals
+    lens = np.array([ld, ld, ld])
+    got = run(smla, dev, x, lens, 500)
+    check_lists(got, x, lens, 500, exact_sets=False)
+
+
+def test_select_workspace_reuse_across_shapes(dev, smla):
+    """The workspace is left ready: calls of different shapes in a row on the
+    same workspace all give valid lists."""
+    note("topk workspace reuse")
+    rng = np.random.default_rng(4)
+    ws = torch.zeros(int(smla.lib.smla_topk_workspace_bytes(16)), dtype=torch.uint8, device=dev)
+    for trial, (B, ld, K) in enumerate([(16, 30000, 2048), (3, 5000, 64), (16, 30000, 2048),
+                                        (9, 70000, 1000), (1, 4, 2)]):
+        x = rng.standard_normal((B, ld)).astype(np.float32)
+        lens = rng.integers(0, ld + 1, size=B)
+        lens[0] = ld
+        out = smla.topk_select(torch.as_tensor(x, device=dev),
+                               torch.as_tensor(lens.astype(np.int32), device=dev), K, workspace=ws)
+        torch.cuda.synchronize(dev)
+        check_lists(out.cpu().numpy(), x, lens, K, exact_sets=True)
+
+
+@pytest.mark.parametrize("name", ["allheads", "million", "ragged"])
+def test_select_full_workloads(dev, smla, name):
+    w = wl.WORKLOADS[name]
+    lens = wl.context_lengths(w, 0)
+    note("topk full %s" % name)
+    scores = wl.index_scores(w, lens, 0, device=dev)
+    out = smla.topk_select(scores, torch.as_tensor(lens.astype(np.int32), device=dev), w.topk)
+    torch.cuda.synchronize(dev)
+    x = scores.cpu().numpy()
+    check_lists(out.cpu().numpy(), x, lens, w.topk, exact_sets=True)
+
+
+def test_select_then_decode(dev, smla):
+    """The selected list feeds the decode: the result equals the oracle's
+    decode over the oracle's list (same set, other order)."""
+    note("topk -> decode")
+    from cases import gpu_cache, oracle_cache, small_case
+    case = small_case(3, 64, [5000, 3000, 900], 2048, seed=81)
+    ld = 5000
+    rng = np.random.default_rng(82)
+    x = rng.standard_normal((3, ld)).astype(np.float32)
+    lens = case["lens"]
+    tk = smla.topk_select(torch.as_tensor(x, device=dev),
+                          torch.as_tensor(lens.astype(np.int32), device=dev), 2048)
+    cache_d = gpu_cache(case, dev, smla)
+    q = to_dev_bf16(case["q"], dev)
+    out, lse = smla.sparse_mla_decode(q, cache_d, torch.as_tensor(case["pt"], device=dev),
+                                      torch.as_tensor(lens.astype(np.int32), device=dev), tk,
+                                      case["scale"])
+    torch.cuda.synchronize(dev)
+    ref_tk = oracle.topk_select(x, lens, 2048)
+    ref_o, ref_l = oracle.sparse_mla_decode(case["q"], oracle_cache(case), case["pt"], lens,
+                                            ref_tk, case["scale"])
+    e_out, e_lse = rel_l2(out.cpu().numpy(), ref_o), lse_err(lse.cpu().numpy(), ref_l)
+    note("  rel_l2 %.3e lse %.3e" % (e_out, e_lse))
+    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
