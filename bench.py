@@ -13,7 +13,9 @@ roofline of the decode kernel, cpu_baseline of the oracle on host cores).
 `--path staged` replaces the fused decode by the staged path (gather-unpack
 of the NVFP4 rows into a lean FP8 copy in HBM, then the FP8 decode over it).
 `--op select` times the top-k select over the workload's synthetic indexer
-scores instead (its own JSON line).
+scores instead, and `--op mtp --tokens T` a multi-token step (T new rows
+appended per sequence, then T queries per sequence, each with its own list);
+each prints its own JSON line.
 """
 from __future__ import annotations
 
@@ -240,6 +242,87 @@ def bench_select(args, w, dev):
     print(json.dumps(result), flush=True)
 
 
+def bench_mtp(args, w, dev):
+    """An MTP verification step: append the T newest rows of every sequence,
+    then decode T query tokens per sequence, each over its own list."""
+    import torch
+    import sparse_mla_decode_amd as smla
+    import workloads as wl
+    T = args.tokens
+    lens = wl.context_lengths(w, args.seed)
+    pt_np, num_pages = wl.build_page_table(w, lens, args.seed)
+    cache = torch.zeros((num_pages, 64, 352), dtype=torch.uint8, device=dev)
+    wl.fill_cache(w, args.seed, lens, pt_np, lambda r, s_: smla.kv_quant_append(r, s_, cache), dev)
+    rows, slots = wl.tail_rows(w, args.seed, lens, pt_np, dev, T)
+    pt = torch.as_tensor(pt_np, device=dev)
+    sl = torch.as_tensor(lens.astype(np.int32), device=dev)
+    per_set = int(sum(min(w.topk, int(L)) for L in lens)) * T * 352
+    sets = args.sets or max(4, math.ceil(2 * CACHE_BYTES_MALL / per_set) + 1)
+    qs, tks, nvalid, nuniq = [], [], [], []
+    for st in range(sets):
+        tk = wl.mtp_topk(w, lens, T, args.seed, st)
+        nvalid.append(int((tk >= 0).sum()))
+        nuniq.append(sum(len(np.unique(tk[b][tk[b] >= 0])) for b in range(w.batch)))
+        tks.append(torch.as_tensor(tk, device=dev))
+        qs.append(torch.cat([wl.queries(w, args.seed, set_id=1000 * st + j, device=dev)[:, None]
+                             for j in range(T)], 1).contiguous())
+    out = torch.empty((w.batch, T, w.heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, T, w.heads), dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(smla.decode_workspace_bytes_mtp(w.batch, T, w.heads, w.topk), 256),
+                     dtype=torch.uint8, device=dev)
+    log("mtp %s T=%d: %d sets, %d rows appended per step" % (w.name, T, sets, rows.shape[0]))
+
+    def step(i, ev=None):
+        st = i % sets
+        if ev is not None:
+            ev[0].record()
+        smla.kv_quant_append(rows, slots, cache)
+        if ev is not None:
+            ev[1].record()
+        smla.sparse_mla_decode_mtp(qs[st], cache, pt, sl, tks[st], w.softmax_scale, out=out,
+                                   lse=lse, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    dec_s = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    used = [(args.warmup + i) % sets for i in range(args.steps)]
+    dec_bytes = float(np.mean([nvalid[u] for u in used])) * 352
+    uniq_bytes = float(np.mean([nuniq[u] for u in used])) * 352
+    flops = float(np.mean([nvalid[u] for u in used])) * w.heads * FLOPS_PER_HEAD_ROW
+    app_bytes = rows.shape[0] * (576 * 2 + 352)
+    gbps = dec_bytes / dec_s / 1e9
+    tflops = flops / dec_s / 1e12
+    result = {
+        "metric": "multi-token sparse NVFP4-MLA decode: effective KV GB/s and queries/sec",
+        "value": round((dec_bytes + app_bytes) / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "tokens": T, "heads": w.heads,
+                   "topk": w.topk, "rotating_sets": sets},
+        "decode_us": round(dec_s * 1e6, 2), "decode_kv_GBps": round(gbps, 1),
+        "unique_rows_frac": round(uniq_bytes / dec_bytes, 4),
+        "decode_tflops": round(tflops, 2),
+        "queries_per_s": round(w.batch * T / (ms * 1e-3), 1),
+        "roofline": ({"bound": "hbm", "achieved": round(uniq_bytes / dec_s / 1e9, 1),
+                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                      "frac": round(uniq_bytes / dec_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None}
+                     if w.heads * FLOPS_PER_HEAD_ROW / 352 < MFMA_F16_PEAK_TFLOPS / HBM_PEAK_GBPS * 1e3
+                     else {"bound": "mfma", "achieved": round(tflops, 2),
+                           "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,8 +331,9 @@ def main():
     ap.add_argument("--workload", default="allheads")
     ap.add_argument("--format", choices=("nvfp4", "fp8"), default="nvfp4",
                     help="cache row format: NVFP4 (352 B) or lean FP8 (576 B)")
-    ap.add_argument("--op", choices=("decode", "select"), default="decode",
-                    help="the decode step (default) or the top-k select alone")
+    ap.add_argument("--op", choices=("decode", "select", "mtp"), default="decode",
+                    help="the decode step (default), the top-k select alone, or an MTP step")
+    ap.add_argument("--tokens", type=int, default=4, help="query tokens per sequence (--op mtp)")
     ap.add_argument("--path", choices=("fused", "staged"), default="fused",
                     help="decode path: the fused kernel, or the staged ablation (NVFP4 only)")
     ap.add_argument("--sets", type=int, default=0, help="rotating (q, top-k) sets (0 = auto)")
@@ -286,6 +370,9 @@ def main():
     w = wl.WORKLOADS[args.workload]
     if args.op == "select":
         bench_select(args, w, dev)
+        return
+    if args.op == "mtp":
+        bench_mtp(args, w, dev)
         return
     fmt = args.format
     if args.path == "staged" and fmt != "nvfp4":

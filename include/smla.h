@@ -219,6 +219,38 @@ int smla_stage_rows_fp8(const uint8_t *cache, int64_t num_pages, const int32_t *
                         void *stream);
 
 /*
+ * ---- Multi-token decode [P5 section 4, "The deployment, spelled out": MTP
+ * speculative decoding with three draft tokens; P1 section "A kernel that
+ * reads four bits directly": several query tokens per launch] ----
+ *
+ * `tokens` query tokens per sequence (the accepted token and its drafts),
+ * each with its own top-k list, over the same NVFP4 cache and page table.
+ * Token j (0-based) of sequence b sits at position seq_lens[b] - tokens + j
+ * and sees positions [0, seq_lens[b] - (tokens - 1 - j)): an entry at or past
+ * that is skipped like any out-of-range entry.  With tokens = 1 this is
+ * smla_sparse_mla_decode.  All tokens of a sequence run on one XCD, so rows
+ * that several of its tokens select are read from that XCD's L2.
+ *
+ *   q             [batch][tokens][heads][576] bf16
+ *   page_table    [batch][max_pages], seq_lens [batch]: per sequence, as above
+ *   topk_indices  [batch][tokens][topk] int32
+ *   out, lse      [batch][tokens][heads][512] fp32, [batch][tokens][heads] fp32
+ *   workspace     smla_decode_workspace_bytes_mtp(batch, tokens, heads, topk)
+ *
+ * Errors as smla_sparse_mla_decode; SMLA_ERR_SHAPE also for tokens not in
+ * [1, 16] or batch * tokens > 65535.
+ */
+size_t smla_decode_workspace_bytes_mtp(int32_t batch, int32_t tokens, int32_t heads,
+                                       int32_t topk);
+
+int smla_sparse_mla_decode_mtp(const void *q_bf16, const uint8_t *cache, int64_t num_pages,
+                               const int32_t *page_table, int32_t max_pages,
+                               const int32_t *seq_lens, const int32_t *topk_indices,
+                               int32_t batch, int32_t tokens, int32_t heads, int32_t topk,
+                               float softmax_scale, float *out, float *lse, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * ---- Top-k select [P1 section "Decode: TP4, and the copies it keeps": an
  * indexer picks the top cached positions, at most 2,048 per query; the
  * prefill-timing figure lists the indexer's logits and top-k as separate

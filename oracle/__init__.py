@@ -235,6 +235,27 @@ def staged_tables(batch: int, topk_len: int):
     return pt, np.full(batch, pp * PAGE_ROWS, dtype=np.int32)
 
 
+def sparse_mla_decode_mtp(q_bf16_bits: np.ndarray, cache: np.ndarray, page_table: np.ndarray,
+                          seq_lens: np.ndarray, topk: np.ndarray, softmax_scale: float,
+                          nthreads: int = 0):
+    """Multi-token decode ("GLM-5.3 PCP/DCP long-context on H200", section 4:
+    MTP speculative decoding with draft tokens): q [B,T,H,576] BF16 bits,
+    topk [B,T,K], page table and seq_lens per sequence.  Token j of sequence
+    b sits at position L_b - T + j and attends over its own list, whose
+    usable entries are those of the decode with length L_b - (T - 1 - j).
+    Returns (out [B,T,H,512], lse [B,T,H]) in fp64."""
+    q = _c(q_bf16_bits, np.uint16)
+    B, T, H, D = q.shape
+    tk = _c(topk, np.int32)
+    assert tk.shape[:2] == (B, T)
+    pt = np.repeat(_c(page_table, np.int32), T, axis=0)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    lens_q = (lens[:, None] - (T - 1 - np.arange(T))[None, :]).reshape(-1)
+    out, lse = sparse_mla_decode(q.reshape(B * T, H, D), cache, pt, lens_q,
+                                 tk.reshape(B * T, -1), softmax_scale, nthreads)
+    return out.reshape(B, T, H, -1), lse.reshape(B, T, H)
+
+
 def topk_select(scores: np.ndarray, seq_lens: np.ndarray, topk: int) -> np.ndarray:
     """[B, ld] float32 scores -> [B, topk] int32: the positions of the
     min(topk, L_b) largest scores of row b (L_b = seq_lens[b] clamped to

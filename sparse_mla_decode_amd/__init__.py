@@ -14,6 +14,8 @@ not been built, importing this package raises.
     stage_rows_fp8, sparse_mla_decode_staged
         the staged path (NVFP4 rows -> FP8 copy in HBM -> FP8 decode), kept
         to measure the fused kernel against
+    sparse_mla_decode_mtp(q [B,T,H,576], cache, page_table, seq_lens, topk [B,T,K], scale)
+        T query tokens per sequence (MTP drafts), each with its own list
     topk_select(scores, seq_lens, topk) -> topk [B,K] int32
         the positions of each query's K largest scores (the decode's list)
 """
@@ -45,7 +47,8 @@ ERRORS = {
 EXPORTS = ("smla_strerror", "smla_version", "smla_kv_quant_append",
            "smla_decode_workspace_bytes", "smla_sparse_mla_decode", "smla_kv_quant_append_fp8",
            "smla_decode_workspace_bytes_fp8", "smla_sparse_mla_decode_fp8",
-           "smla_stage_rows_fp8", "smla_topk_workspace_bytes", "smla_topk_select")
+           "smla_stage_rows_fp8", "smla_decode_workspace_bytes_mtp", "smla_sparse_mla_decode_mtp",
+           "smla_topk_workspace_bytes", "smla_topk_select")
 
 
 class SmlaError(RuntimeError):
@@ -80,6 +83,11 @@ def _load() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.smla_stage_rows_fp8.argtypes = [P, i64, P, i32, P, P, i32, i32, P, P, P]
     lib.smla_stage_rows_fp8.restype = ctypes.c_int
+    lib.smla_decode_workspace_bytes_mtp.argtypes = [i32, i32, i32, i32]
+    lib.smla_decode_workspace_bytes_mtp.restype = sz
+    lib.smla_sparse_mla_decode_mtp.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, i32, f32,
+                                               P, P, P, sz, P]
+    lib.smla_sparse_mla_decode_mtp.restype = ctypes.c_int
     lib.smla_topk_workspace_bytes.argtypes = [i32]
     lib.smla_topk_workspace_bytes.restype = sz
     lib.smla_topk_select.argtypes = [P, i64, P, i32, i32, P, P, sz, P]
@@ -332,3 +340,49 @@ def topk_select(scores: torch.Tensor, seq_lens: torch.Tensor, topk: int,
                                 workspace.numel() * workspace.element_size(),
                                 _stream_ptr(dev, stream)))
     return out
+
+
+def decode_workspace_bytes_mtp(batch: int, tokens: int, heads: int, topk: int) -> int:
+    return int(lib.smla_decode_workspace_bytes_mtp(batch, tokens, heads, topk))
+
+
+def sparse_mla_decode_mtp(q: torch.Tensor, cache: torch.Tensor, page_table: torch.Tensor,
+                          seq_lens: torch.Tensor, topk: torch.Tensor, softmax_scale: float,
+                          out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None, stream=None):
+    """Multi-token decode: q [B,T,H,576] bf16, topk [B,T,K] int32, the page
+    table and seq_lens per sequence (token j sees [0, L_b - (T-1-j))).
+    Returns (out [B,T,H,512] fp32, lse [B,T,H] fp32)."""
+    _req(cache, "cache", torch.uint8, 3)
+    dev = cache.device
+    _req(q, "q", torch.bfloat16, 4, dev)
+    _req(page_table, "page_table", torch.int32, 2, dev)
+    _req(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _req(topk, "topk", torch.int32, 3, dev)
+    B, T, H, D = q.shape
+    if D != DIM:
+        raise ValueError("q must be [B,T,H,576]")
+    if tuple(cache.shape[1:]) != (PAGE_ROWS, ROW_BYTES):
+        raise ValueError("cache must be [num_pages,64,352]")
+    if page_table.shape[0] != B or seq_lens.shape[0] != B or tuple(topk.shape[:2]) != (B, T):
+        raise ValueError("page_table, seq_lens per sequence; topk [B,T,K]")
+    K = topk.shape[2]
+    if out is None:
+        out = torch.empty((B, T, H, LATENT), dtype=torch.float32, device=dev)
+    else:
+        _req(out, "out", torch.float32, 4, dev)
+    if lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    else:
+        _req(lse, "lse", torch.float32, 3, dev)
+    need = decode_workspace_bytes_mtp(B, T, H, K)
+    if workspace is None and need > 0:
+        workspace = workspace_for(dev, need, stream)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.smla_sparse_mla_decode_mtp(q.data_ptr(), cache.data_ptr(), cache.shape[0],
+                                          page_table.data_ptr(), page_table.shape[1],
+                                          seq_lens.data_ptr(), topk.data_ptr(), B, T, H, K,
+                                          float(softmax_scale), out.data_ptr(), lse.data_ptr(),
+                                          ws_ptr, ws_bytes, _stream_ptr(dev, stream)))
+    return out, lse

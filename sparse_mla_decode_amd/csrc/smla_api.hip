@@ -67,19 +67,27 @@ int append_rows(const void *rows_bf16, int64_t n, const int32_t *slot_mapping, u
     return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
-size_t workspace_bytes(int32_t batch, int32_t heads, int32_t topk, smla::RowFormat fmt) {
-    if (batch < 1 || batch > 65535 || (heads != 16 && heads != 64) || topk < 1 ||
+constexpr int32_t kMaxTokens = 16;
+
+bool batch_ok(int32_t batch, int32_t tokens) {
+    return batch >= 1 && tokens >= 1 && tokens <= kMaxTokens && (int64_t)batch * tokens <= 65535;
+}
+
+size_t workspace_bytes(int32_t batch, int32_t tokens, int32_t heads, int32_t topk,
+                       smla::RowFormat fmt) {
+    if (!batch_ok(batch, tokens) || (heads != 16 && heads != 64) || topk < 1 ||
         topk > SMLA_MAX_TOPK)
         return 0;
-    return smla::plan_decode(batch, heads, topk, fmt).workspace_bytes;
+    return smla::plan_decode(batch, tokens, heads, topk, fmt).workspace_bytes;
 }
 
 int decode(const void *q_bf16, const uint8_t *cache, int64_t num_pages, const int32_t *page_table,
            int32_t max_pages, const int32_t *seq_lens, const int32_t *topk_indices, int32_t batch,
-           int32_t heads, int32_t topk, float softmax_scale, float *out, float *lse,
-           void *workspace, size_t workspace_bytes, void *stream, smla::RowFormat fmt) {
+           int32_t tokens, int32_t heads, int32_t topk, float softmax_scale, float *out,
+           float *lse, void *workspace, size_t workspace_bytes, void *stream,
+           smla::RowFormat fmt) {
     if (heads != 16 && heads != 64) return SMLA_ERR_UNSUPPORTED;
-    if (batch < 1 || batch > 65535 || topk < 1 || topk > SMLA_MAX_TOPK || max_pages < 1 ||
+    if (!batch_ok(batch, tokens) || topk < 1 || topk > SMLA_MAX_TOPK || max_pages < 1 ||
         num_pages < 1 || num_pages > ((int64_t)1 << 25))
         return SMLA_ERR_SHAPE;
     if (!q_bf16 || !cache || !page_table || !seq_lens || !topk_indices || !out || !lse)
@@ -87,7 +95,7 @@ int decode(const void *q_bf16, const uint8_t *cache, int64_t num_pages, const in
     if (!aligned(q_bf16, 16) || !aligned(out, 16) || !aligned(cache, 256) || !aligned(lse, 4) ||
         !aligned(page_table, 4) || !aligned(seq_lens, 4) || !aligned(topk_indices, 4))
         return SMLA_ERR_ALIGN;
-    const smla::DecodePlan plan = smla::plan_decode(batch, heads, topk, fmt);
+    const smla::DecodePlan plan = smla::plan_decode(batch, tokens, heads, topk, fmt);
     if (plan.workspace_bytes > 0) {
         if (!workspace || workspace_bytes < plan.workspace_bytes) return SMLA_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return SMLA_ERR_ALIGN;
@@ -96,7 +104,7 @@ int decode(const void *q_bf16, const uint8_t *cache, int64_t num_pages, const in
     if (dev != SMLA_OK) return dev;
     const hipError_t e = smla::launch_sparse_mla_decode(
         static_cast<const uint16_t *>(q_bf16), cache, num_pages, page_table, max_pages, seq_lens,
-        topk_indices, batch, heads, topk, softmax_scale, out, lse, workspace, plan, fmt,
+        topk_indices, batch, tokens, heads, topk, softmax_scale, out, lse, workspace, plan, fmt,
         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
@@ -111,7 +119,7 @@ int smla_kv_quant_append(const void *rows_bf16, int64_t n, const int32_t *slot_m
 }
 
 size_t smla_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t topk) {
-    return workspace_bytes(batch, heads, topk, smla::kFmtNvfp4);
+    return workspace_bytes(batch, 1, heads, topk, smla::kFmtNvfp4);
 }
 
 int smla_sparse_mla_decode(const void *q_bf16, const uint8_t *cache, int64_t num_pages,
@@ -121,7 +129,7 @@ int smla_sparse_mla_decode(const void *q_bf16, const uint8_t *cache, int64_t num
                            float *out, float *lse, void *workspace, size_t workspace_bytes,
                            void *stream) {
     return decode(q_bf16, cache, num_pages, page_table, max_pages, seq_lens, topk_indices, batch,
-                  heads, topk, softmax_scale, out, lse, workspace, workspace_bytes, stream,
+                  1, heads, topk, softmax_scale, out, lse, workspace, workspace_bytes, stream,
                   smla::kFmtNvfp4);
 }
 
@@ -131,7 +139,7 @@ int smla_kv_quant_append_fp8(const void *rows_bf16, int64_t n, const int32_t *sl
 }
 
 size_t smla_decode_workspace_bytes_fp8(int32_t batch, int32_t heads, int32_t topk) {
-    return workspace_bytes(batch, heads, topk, smla::kFmtFp8);
+    return workspace_bytes(batch, 1, heads, topk, smla::kFmtFp8);
 }
 
 int smla_sparse_mla_decode_fp8(const void *q_bf16, const uint8_t *cache, int64_t num_pages,
@@ -141,7 +149,7 @@ int smla_sparse_mla_decode_fp8(const void *q_bf16, const uint8_t *cache, int64_t
                                float *out, float *lse, void *workspace, size_t workspace_bytes,
                                void *stream) {
     return decode(q_bf16, cache, num_pages, page_table, max_pages, seq_lens, topk_indices, batch,
-                  heads, topk, softmax_scale, out, lse, workspace, workspace_bytes, stream,
+                  1, heads, topk, softmax_scale, out, lse, workspace, workspace_bytes, stream,
                   smla::kFmtFp8);
 }
 
@@ -188,6 +196,22 @@ int smla_topk_select(const float *scores, int64_t ld, const int32_t *seq_lens, i
                                                   static_cast<uint32_t *>(workspace),
                                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+size_t smla_decode_workspace_bytes_mtp(int32_t batch, int32_t tokens, int32_t heads,
+                                       int32_t topk) {
+    return workspace_bytes(batch, tokens, heads, topk, smla::kFmtNvfp4);
+}
+
+int smla_sparse_mla_decode_mtp(const void *q_bf16, const uint8_t *cache, int64_t num_pages,
+                               const int32_t *page_table, int32_t max_pages,
+                               const int32_t *seq_lens, const int32_t *topk_indices,
+                               int32_t batch, int32_t tokens, int32_t heads, int32_t topk,
+                               float softmax_scale, float *out, float *lse, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    return decode(q_bf16, cache, num_pages, page_table, max_pages, seq_lens, topk_indices, batch,
+                  tokens, heads, topk, softmax_scale, out, lse, workspace, workspace_bytes,
+                  stream, smla::kFmtNvfp4);
 }
 
 }  // extern "C"

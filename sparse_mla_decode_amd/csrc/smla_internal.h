@@ -37,7 +37,8 @@ struct DecodePlan {
 // Row formats of the decode: the NVFP4 row, or the lean FP8 row.
 enum RowFormat { kFmtNvfp4 = 0, kFmtFp8 = 1 };
 
-DecodePlan plan_decode(int batch, int heads, int topk, RowFormat fmt);
+// batch sequences of `tokens` query tokens each (1 for plain decode)
+DecodePlan plan_decode(int batch, int tokens, int heads, int topk, RowFormat fmt);
 
 hipError_t launch_kv_quant_append(const uint16_t *rows, int64_t n, const int32_t *slots,
                                   uint8_t *cache, int64_t num_pages, hipStream_t stream);
@@ -59,8 +60,8 @@ hipError_t launch_topk_select(const float *scores, int64_t ld, const int32_t *se
 hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int64_t num_pages,
                                     const int32_t *page_table, int32_t max_pages,
                                     const int32_t *seq_lens, const int32_t *topk_idx,
-                                    int32_t batch, int32_t heads, int32_t topk, float scale,
-                                    float *out, float *lse, void *workspace,
+                                    int32_t batch, int32_t tokens, int32_t heads, int32_t topk,
+                                    float scale, float *out, float *lse, void *workspace,
                                     const DecodePlan &plan, RowFormat fmt, hipStream_t stream);
 
 }  // namespace smla

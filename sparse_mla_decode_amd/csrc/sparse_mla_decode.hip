@@ -182,7 +182,8 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                               const int32_t *__restrict__ topk_idx, int32_t heads, int32_t topk,
                               float scale_log2, float *__restrict__ out, float *__restrict__ lse,
                               _Float16 *__restrict__ part_o, float *__restrict__ part_ml,
-                              int32_t batch, int32_t groups, int32_t splits, int32_t per_split) {
+                              int32_t batch, int32_t tokens, int32_t groups, int32_t splits,
+                              int32_t per_split) {
     constexpr int HG = 16 * MB;  // heads of this workgroup
     using R = Ring<FMT>;
     constexpr bool kFp8 = FMT == kFmtFp8;
@@ -217,15 +218,21 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     const int n32 = lane & 31;  // value MFMA: column within a 32-column block / head
     const int g2 = lane >> 5;   // value MFMA: 8-element k group
 
-    // ---- which (sequence, head group, split): consecutive workgroups go to
-    // consecutive XCDs, so all workgroups of sequence b share XCD b % 8 ----
+    // ---- which (query, head group, split): consecutive workgroups go to
+    // consecutive XCDs, so all workgroups of sequence sq -- every head group,
+    // split and query token of it -- share XCD sq % 8 (and rows that several
+    // of its query tokens select are read from that XCD's L2).  Query b is
+    // token j of sequence sq = b / tokens; it sees positions
+    // [0, seq_lens[sq] - (tokens - 1 - j)) ----
     const int id = blockIdx.x;
     const int xcd = id & 7;
     const int rest = id >> 3;
     const int split = rest % splits;
     const int hg = (rest / splits) % groups;
-    const int b = (rest / splits / groups) * 8 + xcd;
-    if (b >= batch) return;
+    const int r_seq = rest / splits / groups;
+    const int sq = (r_seq / tokens) * 8 + xcd;
+    if (sq >= batch) return;
+    const int b = sq * tokens + r_seq % tokens;
     const int unit = b * groups + hg;
     const int e_begin = split * per_split;
     const int e_end = min(topk, e_begin + per_split);
@@ -584,7 +591,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     int cnt_valid = 0, incl = 0;
     {
         const int vt = tid - 256;
-        const int64_t L = seq_lens[b];
+        const int64_t L = (int64_t)seq_lens[sq] - (tokens - 1 - (b - sq * tokens));
         int32_t tv[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -598,7 +605,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
             const int e = e_begin + vt * per_thread + i;
             const int64_t t = tv[i];
             ok[i] = i < per_thread && e < e_end && t >= 0 && t < L && (t >> 6) < max_pages;
-            pv[i] = page_table[(int64_t)b * max_pages + (ok[i] ? (t >> 6) : 0)];
+            pv[i] = page_table[(int64_t)sq * max_pages + (ok[i] ? (t >> 6) : 0)];
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -883,8 +890,8 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 }
 
 // Merge of the splits' partials: one wave per (unit, head), a lane per 8
-// columns; the wave of a head of sequence b runs on XCD b % 8, where the
-// decode workgroups of b wrote the partials (so they are read from that L2).
+// columns; the wave of a head of sequence sq runs on XCD sq % 8, where the
+// decode workgroups of sq wrote the partials (so they are read from that L2).
 // The (m, l) pairs are wave-uniform (scalar loads), every split's loads are
 // issued up front, then combined in split order (fixed, hence
 // deterministic):
@@ -893,12 +900,14 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 __global__ __launch_bounds__(256) void merge_splits_kernel(
     const _Float16 *__restrict__ part_o, const float *__restrict__ part_ml,
     float *__restrict__ out, float *__restrict__ lse, int32_t heads, int32_t hg_size,
-    int32_t groups, int32_t splits, int32_t batch) {
+    int32_t groups, int32_t splits, int32_t batch, int32_t tokens) {
     const int xcd = blockIdx.x & 7;
     const int p = __builtin_amdgcn_readfirstlane((int)(blockIdx.x >> 3) * 4 + (int)(threadIdx.x >> 6));
     const int per_seq = groups * hg_size;
-    const int b = (p / per_seq) * 8 + xcd;
-    if (b >= batch) return;
+    const int r_seq = p / per_seq;
+    const int sq = (r_seq / tokens) * 8 + xcd;
+    if (sq >= batch) return;
+    const int b = sq * tokens + r_seq % tokens;  // query
     const int lane = threadIdx.x & 63;
     const int h = p % hg_size;
     const int unit = b * groups + (p % per_seq) / hg_size;
@@ -943,11 +952,11 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(
 
 }  // namespace
 
-DecodePlan plan_decode(int batch, int heads, int topk, RowFormat fmt) {
+DecodePlan plan_decode(int batch, int tokens, int heads, int topk, RowFormat fmt) {
     DecodePlan p;
     p.heads_per_group = heads >= 32 ? 32 : 16;
     p.groups = heads / p.heads_per_group;
-    const int units = batch * p.groups;
+    const int units = batch * tokens * p.groups;
     const int target = 256;  // one workgroup per CU
     int s = (target + units - 1) / units;
     const int max_s = (topk + kTile - 1) / kTile;
@@ -975,11 +984,11 @@ DecodePlan plan_decode(int batch, int heads, int topk, RowFormat fmt) {
 hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int64_t num_pages,
                                     const int32_t *page_table, int32_t max_pages,
                                     const int32_t *seq_lens, const int32_t *topk_idx,
-                                    int32_t batch, int32_t heads, int32_t topk, float scale,
-                                    float *out, float *lse, void *workspace,
+                                    int32_t batch, int32_t tokens, int32_t heads, int32_t topk,
+                                    float scale, float *out, float *lse, void *workspace,
                                     const DecodePlan &plan, RowFormat fmt, hipStream_t stream) {
-    const int blocks = ((batch + 7) / 8) * 8 * plan.groups * plan.splits;
-    const int units = batch * plan.groups;
+    const int blocks = ((batch + 7) / 8) * 8 * tokens * plan.groups * plan.splits;
+    const int units = batch * tokens * plan.groups;
     _Float16 *part_o = nullptr;
     float *part_ml = nullptr;
     if (plan.splits > 1) {
@@ -993,7 +1002,7 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
 #define SMLA_LAUNCH(MB, FMT)                                                                 \
     hipLaunchKernelGGL((sparse_mla_decode_kernel<MB, FMT>), dim3(blocks), dim3(kThreads), 0, stream, \
                        q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,      \
-                       topk, scale_log2, out, lse, part_o, part_ml, batch, plan.groups,            \
+                       topk, scale_log2, out, lse, part_o, part_ml, batch, tokens, plan.groups,    \
                        plan.splits, plan.per_split)
     if (fmt == kFmtFp8) {
         if (plan.heads_per_group == 32) SMLA_LAUNCH(2, kFmtFp8);
@@ -1005,11 +1014,12 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
 #undef SMLA_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
-    // one wave per (unit, head); the blocks of XCD x take the sequences b = x mod 8
-    const int64_t per_xcd = (int64_t)((batch + 7) / 8) * plan.groups * plan.heads_per_group;
+    // one wave per (unit, head); the blocks of XCD x take the sequences sq = x mod 8
+    const int64_t per_xcd =
+        (int64_t)((batch + 7) / 8) * tokens * plan.groups * plan.heads_per_group;
     hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)(8 * ((per_xcd + 3) / 4))), dim3(256), 0,
                        stream, part_o, part_ml, out, lse, heads, plan.heads_per_group,
-                       plan.groups, plan.splits, batch);
+                       plan.groups, plan.splits, batch, tokens);
     return hipGetLastError();
 }
 

@@ -1,0 +1,135 @@
+"""GPU parity of the multi-token (MTP) decode against the CPU oracle, through
+the C ABI.  Same bars as the single-token decode: out within 2e-2 relative L2
+over the whole [B,T,H,512] tensor, lse within 1e-3 absolute.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from cases import gpu_cache, lse_err, note, oracle_cache, rel_l2, small_case, to_dev_bf16
+from test_gpu_parity import LSE_TOL, OUT_TOL
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def smla():
+    import sparse_mla_decode_amd as m
+    return m
+
+
+def mtp_case(batch, tokens, heads, lens, topk, seed):
+    """small_case rows and page table; T queries per sequence; token 0's list
+    over the positions it sees, drafts swap 1 entry in 8, and every list also
+    holds the newest positions (some of which a token may not see)."""
+    case = small_case(batch, heads, lens, topk, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    q = wl.bf16_bits(torch.randn((batch, tokens, heads, 576),
+                                 generator=torch.Generator().manual_seed(seed + 2)).to(torch.bfloat16))
+    tk = np.full((batch, tokens, topk), -1, dtype=np.int32)
+    for b in range(batch):
+        L = int(case["lens"][b])
+        base = case["topk"][b].copy()
+        base[base >= L - tokens + 1] = -1
+        for j in range(tokens):
+            row = base.copy()
+            valid = np.flatnonzero(row >= 0)
+            m = valid.size // 8 if j else 0
+            if m:
+                row[rng.choice(valid, size=m, replace=False)] = rng.integers(0, max(L - tokens + 1 + j, 1), m)
+            newest = np.arange(max(L - tokens, 0), L, dtype=np.int32)   # visible or not
+            free = np.flatnonzero(row < 0)[:newest.size]
+            row[free] = newest[:free.size]
+            tk[b, j] = row
+    case["q"] = q
+    case["topk"] = tk
+    return case
+
+
+MTP_CASES = [
+    (2, 2, 16, [3000, 900], 512),
+    (3, 4, 64, [5000, 2000, 300], 2048),
+    (1, 3, 16, [70000], 2048),
+    (5, 2, 64, [64, 65, 129, 2, 4000], 64),
+    (4, 4, 16, [2500, 2500, 90, 700], 2048),
+]
+
+
+@pytest.mark.parametrize("batch,tokens,heads,lens,topk", MTP_CASES,
+                         ids=["B%d_T%d_H%d_K%d" % (c[0], c[1], c[2], c[4]) for c in MTP_CASES])
+def test_mtp_matches_oracle(dev, smla, batch, tokens, heads, lens, topk):
+    case = mtp_case(batch, tokens, heads, lens, topk, seed=batch * 7 + tokens + topk)
+    note("mtp B=%d T=%d H=%d lens=%s K=%d" % (batch, tokens, heads, lens, topk))
+    cache_d = gpu_cache(case, dev, smla)
+    cache_o = oracle_cache(case)
+    out, lse = smla.sparse_mla_decode_mtp(
+        to_dev_bf16(case["q"], dev), cache_d, torch.as_tensor(case["pt"], device=dev),
+        torch.as_tensor(case["lens"].astype(np.int32), device=dev),
+        torch.as_tensor(case["topk"], device=dev), case["scale"])
+    torch.cuda.synchronize(dev)
+    ref_o, ref_l = oracle.sparse_mla_decode_mtp(case["q"], cache_o, case["pt"], case["lens"],
+                                                case["topk"], case["scale"])
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    e_out, e_lse = rel_l2(out, ref_o), lse_err(lse, ref_l)
+    note("  rel_l2 %.3e lse %.3e" % (e_out, e_lse))
+    assert np.isfinite(out).all()
+    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+
+
+def test_mtp_one_token_is_the_plain_decode(dev, smla):
+    note("mtp T=1 vs plain decode")
+    case = small_case(3, 64, [3000, 2000, 700], 2048, seed=91)
+    cache_d = gpu_cache(case, dev, smla)
+    args = (cache_d, torch.as_tensor(case["pt"], device=dev),
+            torch.as_tensor(case["lens"].astype(np.int32), device=dev))
+    q = to_dev_bf16(case["q"], dev)
+    tk = torch.as_tensor(case["topk"], device=dev)
+    o1, l1 = smla.sparse_mla_decode(q, *args, tk, case["scale"])
+    o2, l2 = smla.sparse_mla_decode_mtp(q[:, None].contiguous(), *args, tk[:, None].contiguous(),
+                                        case["scale"])
+    torch.cuda.synchronize(dev)
+    assert torch.equal(o1, o2[:, 0]) and torch.equal(l1, l2[:, 0])
+
+
+@pytest.mark.parametrize("name,tokens,sample", [("tp4", 4, [0, 31]), ("allheads", 2, [0, 63])])
+def test_mtp_full_workload_sampled(dev, smla, name, tokens, sample):
+    w = wl.WORKLOADS[name]
+    lens = wl.context_lengths(w, 0)
+    pt_np, num_pages = wl.build_page_table(w, lens, 0)
+    note("mtp full %s T=%d" % (name, tokens))
+    cache = torch.zeros((num_pages, 64, 352), dtype=torch.uint8, device=dev)
+    wl.fill_cache(w, 0, lens, pt_np, lambda r, s: smla.kv_quant_append(r, s, cache), dev)
+    tk = wl.mtp_topk(w, lens, tokens, 0)
+    q = torch.cat([wl.queries(w, 0, set_id=j, device=dev)[:, None] for j in range(tokens)], 1)
+    out, lse = smla.sparse_mla_decode_mtp(q.contiguous(), cache, torch.as_tensor(pt_np, device=dev),
+                                          torch.as_tensor(lens.astype(np.int32), device=dev),
+                                          torch.as_tensor(tk, device=dev), w.softmax_scale)
+    torch.cuda.synchronize(dev)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    qbits = wl.bf16_bits(q)
+    for b in sample:
+        for j in range(tokens):
+            sel = tk[b, j][tk[b, j] >= 0].astype(np.int64)
+            rows = oracle.quant_rows(wl.bf16_bits(wl.rows_at(w, 0, b, sel, device=dev)))
+            n = sel.size
+            mini = np.zeros(((n + 63) // 64, 64, 352), dtype=np.uint8)
+            mini.reshape(-1, 352)[:n] = rows
+            ro, rl = oracle.sparse_mla_decode(qbits[b, j][None], mini,
+                                              np.arange(mini.shape[0], dtype=np.int32)[None],
+                                              np.array([n]), np.arange(n, dtype=np.int32)[None],
+                                              w.softmax_scale)
+            e_out, e_lse = rel_l2(out[b, j][None], ro), lse_err(lse[b, j][None], rl)
+            note("  seq %d token %d: rel_l2 %.3e lse %.3e" % (b, j, e_out, e_lse))
+            assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+    del cache
+    torch.cuda.empty_cache()

@@ -26,6 +26,9 @@ Recipe (stated once here, repeated in the design notes):
   * Top-k lists: ``uniform`` = min(K, L) distinct positions uniform over
     [0, L); ``recent`` = K/2 distinct from the last 6000 positions and K/2
     from the rest.  Lists are shuffled (never sorted) and padded with -1 to K.
+  * Multi-token (MTP) lists: token 0 takes the workload's list over the
+    positions it sees; each draft token j swaps 1 entry in 8 for a fresh
+    position among the ones it sees (see ``mtp_topk``).
   * Indexer scores (input of the top-k select): N(0,1) fp32 per position;
     for ``recent`` workloads the last 6000 positions get +RECENT_SHIFT, which
     puts about half of the top 2048 of a 140K context in that window (the
@@ -163,6 +166,40 @@ def topk_indices(w: Workload, lens: np.ndarray, seed: int = 0, set_id: int = 0,
             idx = rng.choice(L, size=n, replace=False)
         out[b, :idx.size] = idx.astype(np.int32)
     return out
+
+
+MTP_REPLACE = 8     # a draft token's list differs from token 0's in 1 of 8 entries
+
+
+def mtp_topk(w: Workload, lens: np.ndarray, tokens: int, seed: int = 0,
+             set_id: int = 0) -> np.ndarray:
+    """[B, T, K] lists of T query tokens per sequence (the accepted token and
+    its drafts).  Token 0's list is the workload's list over the positions it
+    sees, [0, L - T + 1); token j's list is token 0's with 1 entry in
+    MTP_REPLACE swapped for a distinct position drawn from [0, L - T + 1 + j)
+    (so drafts share most rows, and may select the newest positions)."""
+    B, K = len(lens), w.topk
+    base = topk_indices(w, np.maximum(np.asarray(lens) - (tokens - 1), 0), seed, set_id)
+    out = np.repeat(base[:, None, :], tokens, axis=1)
+    for b in range(B):
+        L = int(lens[b])
+        for j in range(1, tokens):
+            rng = _rng(seed, 6, set_id, b, j)
+            row = out[b, j]
+            valid = np.flatnonzero(row >= 0)
+            vis = max(L - (tokens - 1) + j, 0)
+            m = valid.size // MTP_REPLACE
+            if m == 0 or vis <= valid.size:
+                continue
+            taken = set(row[valid].tolist())
+            fresh = []
+            while len(fresh) < m:
+                t = int(rng.integers(0, vis))
+                if t not in taken:
+                    taken.add(t)
+                    fresh.append(t)
+            row[rng.choice(valid, size=m, replace=False)] = fresh
+    return out.astype(np.int32)
 
 
 def outlier_channels(w: Workload, seed: int = 0) -> np.ndarray:
