@@ -101,7 +101,7 @@ def summarize_kernel_stats(d):
         # demangled (smla::(anonymous namespace)::k<2, 1>(...)) or mangled
         # (_ZN4smla12_GLOBAL__N_11kILi2ELi1EEEv...) names -> k or k<2, 1>
         m = re.search(r"(kv_quant_append(?:_fp8)?_kernel|sparse_mla_decode_kernel|"
-                      r"stage_rows_fp8_kernel|topk_hist_kernel|topk_gather_kernel|"
+                      r"stage_rows_fp8_kernel|topk_hist_kernel|topk_split_kernel|topk_finish_kernel|"
                       r"merge_splits_kernel)(I(?:Li-?\d+E)+E|<[^>]*>)?", name)
         if not m:
             continue
@@ -196,7 +196,7 @@ def bench_select(args, w, dev):
     sets = args.sets or max(2, math.ceil(2 * CACHE_BYTES_MALL / set_bytes) + 1)
     scores = [first] + [wl.index_scores(w, lens, args.seed, s, device=dev) for s in range(1, sets)]
     out = torch.empty((w.batch, w.topk), dtype=torch.int32, device=dev)
-    ws = smla.topk_workspace(dev, w.batch)
+    ws = smla.topk_workspace(dev, w.batch, first.shape[1])
     log("select %s: %d x %d scores, %d rotating sets" % (w.name, w.batch, first.shape[1], sets))
     for i in range(args.warmup):
         smla.topk_select(scores[i % sets], sl, w.topk, out=out, workspace=ws)

@@ -266,17 +266,17 @@ int smla_sparse_mla_decode_mtp(const void *q_bf16, const uint8_t *cache, int64_t
  *   scores        [batch][ld] fp32, device, 16-B aligned, ld a multiple of 4
  *   seq_lens      [batch] int32, device
  *   topk_indices  [batch][topk] int32, device (output)
- *   workspace     smla_topk_workspace_bytes(batch) bytes, 256-B aligned.  It
- *                 must be zero-filled before its first use; every call that
- *                 returns SMLA_OK leaves it ready for the next call with any
- *                 shape.  Calls that share a workspace must not overlap.
+ *   workspace     smla_topk_workspace_bytes(batch, ld) bytes, 256-B aligned.
+ *                 It must be zero-filled before its first use; every call
+ *                 leaves it all zero again, ready for a call of any shape.
+ *                 Calls that share a workspace must not overlap.
  *
  * Errors: SMLA_ERR_SHAPE (batch not in [1, 65535], topk not in [1, 2048], ld
  * not a multiple of 4 in [4, 2^30]), SMLA_ERR_NULL, SMLA_ERR_ALIGN,
  * SMLA_ERR_WORKSPACE (missing or short), SMLA_ERR_DEVICE, SMLA_ERR_LAUNCH.
- * Asynchronous on `stream`; four kernel launches; nothing is allocated.
+ * Asynchronous on `stream`; three kernel launches; nothing is allocated.
  */
-size_t smla_topk_workspace_bytes(int32_t batch);
+size_t smla_topk_workspace_bytes(int32_t batch, int64_t ld);
 
 int smla_topk_select(const float *scores, int64_t ld, const int32_t *seq_lens, int32_t batch,
                      int32_t topk, int32_t *topk_indices, void *workspace, size_t workspace_bytes,

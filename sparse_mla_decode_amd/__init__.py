@@ -88,7 +88,7 @@ def _load() -> ctypes.CDLL:
     lib.smla_sparse_mla_decode_mtp.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, i32, f32,
                                                P, P, P, sz, P]
     lib.smla_sparse_mla_decode_mtp.restype = ctypes.c_int
-    lib.smla_topk_workspace_bytes.argtypes = [i32]
+    lib.smla_topk_workspace_bytes.argtypes = [i32, i64]
     lib.smla_topk_workspace_bytes.restype = sz
     lib.smla_topk_select.argtypes = [P, i64, P, i32, i32, P, P, sz, P]
     lib.smla_topk_select.restype = ctypes.c_int
@@ -302,10 +302,10 @@ def sparse_mla_decode_staged(q: torch.Tensor, cache: torch.Tensor, page_table: t
 _topk_workspaces: dict = {}
 
 
-def topk_workspace(device: torch.device, batch: int, stream=None) -> torch.Tensor:
-    """A zero-filled top-k workspace for at least `batch` queries, cached per
-    (device, stream); the select leaves it ready for the next call."""
-    need = int(lib.smla_topk_workspace_bytes(batch))
+def topk_workspace(device: torch.device, batch: int, ld: int, stream=None) -> torch.Tensor:
+    """A zero-filled top-k workspace for `batch` rows of `ld` scores, cached
+    per (device, stream); every select leaves it all zero again."""
+    need = int(lib.smla_topk_workspace_bytes(batch, ld))
     key = (device.index, _stream_ptr(device, stream))
     with _ws_lock:
         ws = _topk_workspaces.get(key)
@@ -334,7 +334,7 @@ def topk_select(scores: torch.Tensor, seq_lens: torch.Tensor, topk: int,
         if tuple(out.shape) != (B, topk):
             raise ValueError("out must be [B, topk]")
     if workspace is None:
-        workspace = topk_workspace(dev, B, stream)
+        workspace = topk_workspace(dev, B, ld, stream)
     _check(lib.smla_topk_select(scores.data_ptr(), ld, seq_lens.data_ptr(), B, int(topk),
                                 out.data_ptr(), workspace.data_ptr(),
                                 workspace.numel() * workspace.element_size(),

@@ -173,9 +173,9 @@ int smla_stage_rows_fp8(const uint8_t *cache, int64_t num_pages, const int32_t *
     return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
-size_t smla_topk_workspace_bytes(int32_t batch) {
-    if (batch < 1 || batch > 65535) return 0;
-    return (size_t)batch * (size_t)smla::topk_workspace_stride() * sizeof(uint32_t);
+size_t smla_topk_workspace_bytes(int32_t batch, int64_t ld) {
+    if (batch < 1 || batch > 65535 || ld < 1 || ld > ((int64_t)1 << 30)) return 0;
+    return (size_t)batch * (size_t)smla::topk_workspace_stride(ld) * sizeof(uint32_t);
 }
 
 int smla_topk_select(const float *scores, int64_t ld, const int32_t *seq_lens, int32_t batch,
@@ -187,7 +187,8 @@ int smla_topk_select(const float *scores, int64_t ld, const int32_t *seq_lens, i
     if (!scores || !seq_lens || !topk_indices) return SMLA_ERR_NULL;
     if (!aligned(scores, 16) || !aligned(seq_lens, 4) || !aligned(topk_indices, 4))
         return SMLA_ERR_ALIGN;
-    if (!workspace || workspace_bytes < smla_topk_workspace_bytes(batch)) return SMLA_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < smla_topk_workspace_bytes(batch, ld))
+        return SMLA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return SMLA_ERR_ALIGN;
     if ((int64_t)batch * ((ld + 4095) / 4096) > INT32_MAX) return SMLA_ERR_SHAPE;
     const int dev = device_ok();

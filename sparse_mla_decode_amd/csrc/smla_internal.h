@@ -52,7 +52,7 @@ hipError_t launch_stage_rows_fp8(const uint8_t *cache, int64_t num_pages,
                                  hipStream_t stream);
 
 // top-k select: uint32 words of workspace per query, and the launches
-int64_t topk_workspace_stride();
+int64_t topk_workspace_stride(int64_t ld);
 hipError_t launch_topk_select(const float *scores, int64_t ld, const int32_t *seq_lens,
                               int32_t batch, int32_t topk, int32_t *out, uint32_t *ws,
                               hipStream_t stream);

@@ -158,9 +158,11 @@ def test_stage_rejects_bad_arguments():
 
 def test_topk_select_rejects_bad_arguments():
     import sparse_mla_decode_amd as smla
-    assert smla.lib.smla_topk_workspace_bytes(0) == 0
-    ws1 = smla.lib.smla_topk_workspace_bytes(1)
-    assert ws1 >= 4 * (2048 + 2048 + 1024) and smla.lib.smla_topk_workspace_bytes(10) == 10 * ws1
+    assert smla.lib.smla_topk_workspace_bytes(0, 4096) == 0
+    assert smla.lib.smla_topk_workspace_bytes(1, 0) == 0
+    ws1 = smla.lib.smla_topk_workspace_bytes(1, 4096)
+    assert ws1 >= 4 * 2048 + 8 * 4096 and ws1 % 256 == 0
+    assert smla.lib.smla_topk_workspace_bytes(10, 4096) == 10 * ws1
 
     def tk(**kw):
         a = dict(scores=FAKE, ld=4096, seq_lens=FAKE, batch=2, topk=2048, out=FAKE, ws=FAKE,

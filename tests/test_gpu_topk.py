@@ -95,7 +95,8 @@ def test_select_workspace_reuse_across_shapes(dev, smla):
     same workspace all give valid lists."""
     note("topk workspace reuse")
     rng = np.random.default_rng(4)
-    ws = torch.zeros(int(smla.lib.smla_topk_workspace_bytes(16)), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(int(smla.lib.smla_topk_workspace_bytes(16, 70000)), dtype=torch.uint8,
+                     device=dev)
     for trial, (B, ld, K) in enumerate([(16, 30000, 2048), (3, 5000, 64), (16, 30000, 2048),
                                         (9, 70000, 1000), (1, 4, 2)]):
         x = rng.standard_normal((B, ld)).astype(np.float32)
@@ -105,6 +106,21 @@ def test_select_workspace_reuse_across_shapes(dev, smla):
                                torch.as_tensor(lens.astype(np.int32), device=dev), K, workspace=ws)
         torch.cuda.synchronize(dev)
         check_lists(out.cpu().numpy(), x, lens, K, exact_sets=True)
+        assert not ws.any(), "the select leaves its workspace all zero"
+
+
+def test_select_overflowing_candidates(dev, smla):
+    """More keys in the threshold's first-digit bin than the candidate buffer
+    holds (16384): the finish reads them from the scores."""
+    note("topk candidate overflow")
+    rng = np.random.default_rng(5)
+    ld = 40000
+    x = np.full((3, ld), 1.0, dtype=np.float32)               # all in one bin
+    x[1] = 1.0 + rng.integers(0, 64, ld).astype(np.float32) / 1024.0   # one bin, 64 values
+    x[2] = rng.standard_normal(ld).astype(np.float32)
+    lens = np.array([ld, ld - 3, ld])
+    got = run(smla, dev, x, lens, 2048)
+    check_lists(got, x, lens, 2048, exact_sets=False)
 
 
 @pytest.mark.parametrize("name", ["allheads", "million", "ragged"])
