@@ -49,10 +49,10 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """First 16 hex digits of the sha256 of the decode kernels' source file."""
     h = hashlib.sha256()
-    for name in ("sparse_mla_decode.hip", "smla_internal.h"):
-        with open(os.path.join(ROOT, "sparse_mla_decode_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    with open(os.path.join(ROOT, "sparse_mla_decode_amd", "csrc", "sparse_mla_decode.hip"), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
