@@ -102,12 +102,12 @@ def summarize_kernel_stats(d):
         # (_ZN4smla12_GLOBAL__N_11kILi2ELi1EEEv...) names -> k or k<2, 1>
         m = re.search(r"(kv_quant_append(?:_fp8)?_kernel|sparse_mla_decode_kernel|"
                       r"stage_rows_fp8_kernel|topk_hist_kernel|topk_split_kernel|topk_finish_kernel|"
-                      r"merge_splits_kernel)(I(?:Li-?\d+E)+E|<[^>]*>)?", name)
+                      r"merge_splits_kernel)(I(?:L[ib]-?\d+E)+E|<[^>]*>)?", name)
         if not m:
             continue
         targs = m.group(2) or ""
         if targs.startswith("I"):
-            targs = "<%s>" % ", ".join(re.findall(r"Li(-?\d+)E", targs))
+            targs = "<%s>" % ", ".join(re.findall(r"L[ib](-?\d+)E", targs))
         short = m.group(1) + targs
         out.append("%-60s %8s %12.3f %12.3f %12.3f" % (
             short[:60], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
@@ -320,6 +320,38 @@ def bench_mtp(args, w, dev):
                            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}),
     }
+    if not args.no_cpu:
+        import oracle
+        tk0 = tks[0].cpu().numpy()
+        qb = wl.bf16_bits(qs[0])
+        cores = min(len(os.sched_getaffinity(0)), 16)
+        t_used, done, kvb = 0.0, 0, 0
+        for b in range(w.batch):
+            sel_all = [tk0[b, j][tk0[b, j] >= 0].astype(np.int64) for j in range(T)]
+            uniq = np.unique(np.concatenate(sel_all))
+            rows_ = oracle.quant_rows(wl.bf16_bits(wl.rows_at(w, args.seed, b, uniq, device=dev)))
+            n = uniq.size
+            mini = np.zeros(((n + 63) // 64, 64, 352), dtype=np.uint8)
+            mini.reshape(-1, 352)[:n] = rows_
+            where = {int(t): i for i, t in enumerate(uniq)}
+            tk_m = np.full((1, T, w.topk), -1, dtype=np.int32)
+            for j in range(T):
+                tk_m[0, j, :sel_all[j].size] = [where[int(t)] for t in sel_all[j]]
+            t0 = time.perf_counter()
+            # every selected row is visible to its token here: lengths n + T - 1
+            oracle.sparse_mla_decode_mtp(qb[b:b + 1], mini,
+                                         np.arange(mini.shape[0], dtype=np.int32)[None],
+                                         np.array([n + T - 1]), tk_m, w.softmax_scale,
+                                         nthreads=cores)
+            t_used += time.perf_counter() - t0
+            done += 1
+            kvb += sum(x.size for x in sel_all) * 352
+            if t_used >= args.cpu_budget:
+                break
+        result["cpu_baseline"] = {
+            "value": round(kvb / t_used / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "oracle multi-token decode (fp64 C, OpenMP over heads) of %d of %d "
+                      "sequences x %d tokens, %.1f s" % (done, w.batch, T, t_used)}
     print(json.dumps(result), flush=True)
 
 

@@ -133,3 +133,52 @@ def test_mtp_full_workload_sampled(dev, smla, name, tokens, sample):
             assert e_out <= OUT_TOL and e_lse <= LSE_TOL
     del cache
     torch.cuda.empty_cache()
+
+
+def test_mtp_edge_cases(dev, smla):
+    """Draft tokens whose lists share only some rows, a token with no usable
+    entry, rows repeated in both lists, an empty first token."""
+    note("mtp edge cases")
+    case = small_case(4, 16, [3000, 3000, 2000, 1500], 1024, seed=95)
+    T = 2
+    rng = np.random.default_rng(96)
+    q = wl.bf16_bits(torch.randn((4, T, 16, 576), generator=torch.Generator().manual_seed(97))
+                     .to(torch.bfloat16))
+    tk = np.full((4, T, 1024), -1, dtype=np.int32)
+    a = rng.choice(2999, 400, replace=False).astype(np.int32)
+    # seq 0: token 1 shares only token 0's later rows
+    tk[0, 0, :400] = a
+    tk[0, 1, :300] = a[100:]
+    # seq 1: token 1 selects nothing usable (beyond its length or -1)
+    tk[1, 0, :400] = a
+    tk[1, 1, :5] = [3000, 3001, -1, -7, 10 ** 6]
+    # seq 2: repeated rows: token 0 twice, token 1 three times, plus others
+    r = np.arange(0, 1990, 10, dtype=np.int32)
+    tk[2, 0, :199] = r
+    tk[2, 0, 199:201] = [5, 5]
+    tk[2, 1, :199] = r[::-1]
+    tk[2, 1, 199:202] = [5, 5, 5]
+    tk[2, 1, 202:300] = rng.integers(0, 1999, 98)
+    # seq 3: token 0 empty, token 1 sees the newest position too
+    tk[3, 1, :700] = rng.choice(1500, 700, replace=False)
+    tk[3, 1, 700] = 1499
+    case["q"], case["topk"] = q, tk
+    cache_d = gpu_cache(case, dev, smla)
+    cache_o = oracle_cache(case)
+    out, lse = smla.sparse_mla_decode_mtp(
+        to_dev_bf16(q, dev), cache_d, torch.as_tensor(case["pt"], device=dev),
+        torch.as_tensor(case["lens"].astype(np.int32), device=dev), torch.as_tensor(tk, device=dev),
+        case["scale"])
+    torch.cuda.synchronize(dev)
+    ref_o, ref_l = oracle.sparse_mla_decode_mtp(q, cache_o, case["pt"], case["lens"], tk, case["scale"])
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(out).all()
+    assert np.isneginf(lse[1, 1]).all() and not out[1, 1].any()
+    assert np.isneginf(lse[3, 0]).all() and not out[3, 0].any()
+    e_out, e_lse = rel_l2(out, ref_o), lse_err(lse, ref_l)
+    note("  rel_l2 %.3e lse %.3e" % (e_out, e_lse))
+    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+    for b in range(4):
+        for j in range(T):
+            if np.isfinite(ref_l[b, j]).all():
+                assert rel_l2(out[b, j], ref_o[b, j]) <= OUT_TOL, (b, j)
