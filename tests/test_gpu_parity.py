@@ -407,3 +407,40 @@ def test_decode_ignores_unselected_nan_row(dev, smla, fmt):
     e_out, e_lse = rel_l2(out, ref_o), lse_err(lse, ref_l)
     note("  rel_l2 %.3e lse %.3e" % (e_out, e_lse))
     assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+
+
+def test_decode_max_batch(dev, smla):
+    """The largest batch the ABI takes: 65,535 sequences of 64 heads, so that
+    element offsets into q, out and lse pass 2^31; each sequence one page
+    (of a global permutation) and a list of its 64 tokens with padding;
+    sampled sequences against the oracle."""
+    B, H, K, L = 65535, 64, 80, 64
+    note("decode max batch B=%d H=%d" % (B, H))
+    g = torch.Generator(device=dev)
+    g.manual_seed(123)
+    perm = torch.randperm(B + 3, generator=g, device=dev)[:B].to(torch.int32)
+    pt = perm[:, None].contiguous()                                  # page of sequence b
+    rows = torch.randn((B * L, 576), generator=g, device=dev).to(torch.bfloat16)
+    slots = (pt.to(torch.int64) * 64 + torch.arange(64, device=dev)[None, :]).reshape(-1)
+    cache = torch.zeros((B + 3, 64, 352), dtype=torch.uint8, device=dev)
+    smla.kv_quant_append(rows, slots.to(torch.int32), cache)
+    q = torch.randn((B, H, 576), generator=g, device=dev).to(torch.bfloat16)
+    order = torch.argsort(torch.rand((B, L), generator=g, device=dev), dim=1).to(torch.int32)
+    tk = torch.full((B, K), -1, dtype=torch.int32, device=dev)
+    tk[:, 3:3 + L] = order
+    sl = torch.full((B,), L, dtype=torch.int32, device=dev)
+    out, lse = smla.sparse_mla_decode(q, cache, pt, sl, tk, 1.0 / np.sqrt(576.0))
+    torch.cuda.synchronize(dev)
+    assert torch.isfinite(out).all().item() and torch.isfinite(lse).all().item()
+    for b in (0, 1, 32767, B - 2, B - 1):
+        rb = wl.bf16_bits(rows[b * L:(b + 1) * L])
+        mini = oracle.quant_rows(rb).reshape(1, 64, 352)
+        got_bytes = cache[int(pt[b, 0])].cpu().numpy()
+        assert np.array_equal(got_bytes, mini[0]), "cache bytes differ for sequence %d" % b
+        ro, rl = oracle.sparse_mla_decode(wl.bf16_bits(q[b:b + 1]), mini, np.zeros((1, 1), np.int32),
+                                          np.array([L]), tk[b:b + 1].cpu().numpy(), 1.0 / np.sqrt(576.0))
+        e_out, e_lse = rel_l2(out[b:b + 1].cpu().numpy(), ro), lse_err(lse[b:b + 1].cpu().numpy(), rl)
+        note("  seq %d: rel_l2 %.3e lse %.3e" % (b, e_out, e_lse))
+        assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+    del rows, q, out, lse, cache
+    torch.cuda.empty_cache()
