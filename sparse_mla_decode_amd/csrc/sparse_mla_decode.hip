@@ -870,7 +870,9 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     }
     // split: the normalised partial (f16) and its (m, l) for the merge
     // kernel.  Layout: part_o [unit][split][HG][512], part_ml
-    // [unit][split][HG][2] = (running max in log2 units, sum)
+    // [unit][split][HG][2] = (running max in log2 units, sum).  The partials
+    // are streamed past the L2 (non-temporal stores), which leaves the L2 to
+    // the rows still being gathered.
     const size_t pidx = (size_t)unit * splits + split;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -880,7 +882,8 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         _Float16 *prow = part_o + (pidx * HG + h) * kLatent + 128 * sw + n32;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) prow[32 * cb] = (_Float16)(o[cb][i] * inv);
+        for (int cb = 0; cb < 4; ++cb)
+            __builtin_nontemporal_store((_Float16)(o[cb][i] * inv), &prow[32 * cb]);
     }
     if (vt < HG) {
         const float l_tot = sum_lds[0][vt] + sum_lds[1][vt] + sum_lds[2][vt] + sum_lds[3][vt];
