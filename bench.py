@@ -147,6 +147,48 @@ def summarize_counters(fetch_dir, write_dir, workload):
     return "\n".join(lines)
 
 
+def summarize_pmc(dirs):
+    """Per-kernel averages per dispatch of the counters in one or more
+    rocprofv3 --pmc directories, and what they imply.  GRBM_GUI_ACTIVE as
+    collected is the sum over the 8 XCDs' GRBM instances, so one XCD's busy
+    cycles are a eighth of it.  MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES /
+    (one XCD's GRBM_GUI_ACTIVE x 1024 SIMDs); LDS bank-conflict share =
+    SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; per-wave issue shares =
+    SQ_ACTIVE_INST_x / SQ_WAVE_CYCLES (both counted per wave)."""
+    import re
+    per = {}
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            m = re.search(r"(sparse_mla_decode_kernel|merge_splits_kernel|kv_quant_append(?:_fp8)?_kernel|"
+                          r"stage_rows_fp8_kernel|topk_hist_kernel|topk_split_kernel|topk_finish_kernel)",
+                          r["Kernel_Name"])
+            if not m:
+                continue
+            per.setdefault(m.group(1), {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    out = []
+    for k, cs in sorted(per.items()):
+        out.append(k)
+        avg = {c: sum(v) / len(v) for c, v in cs.items()}
+        for c in sorted(avg):
+            out.append("  %-28s %16.1f  (%d dispatches)" % (c, avg[c], len(cs[c])))
+        g = avg.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+        if g:
+            out.append("  => one XCD busy %.0f cycles" % g)
+        if g and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            out.append("  => MFMA busy %.1f%% of SIMD cycles" % (100 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * 1024)))
+        if avg.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in avg:
+            out.append("  => LDS bank conflicts %.1f%% of LDS active cycles"
+                       % (100 * avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_LDS_IDX_ACTIVE"]))
+        wc = avg.get("SQ_WAVE_CYCLES")
+        if wc:
+            for c in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY",
+                      "SQ_WAIT_ANY"):
+                if c in avg:
+                    out.append("  => %s %.1f%% of wave cycles" % (c, 100 * avg[c] / wc))
+    return "\n".join(out)
+
+
 def cpu_baseline(w, seed, lens, tk_np, qbits, budget_s, dev, fmt):
     """Time the oracle's decode on host cores over as many sequences as fit in
     roughly budget_s seconds (at least one)."""
@@ -376,12 +418,17 @@ def main():
                     help="run y = -x over 256 MiB first (HBM counter calibration)")
     ap.add_argument("--summarize-kernel-stats", metavar="DIR",
                     help="print a summary of a rocprofv3 --kernel-trace --stats directory")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="print per-kernel counter averages of rocprofv3 --pmc directories")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print HBM bytes per decode call from FETCH_SIZE / WRITE_SIZE runs")
     args = ap.parse_args()
 
     if args.summarize_kernel_stats:
         print(summarize_kernel_stats(args.summarize_kernel_stats))
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
         return
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters,

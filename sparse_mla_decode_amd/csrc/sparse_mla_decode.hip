@@ -96,6 +96,13 @@ template <> struct Ring<kFmtFp8> {
 // banks instead of the two that a 576-byte row stride leaves them.
 __device__ __forceinline__ int fp8_swz(int r) { return ((r >> 1) & 3) << 1; }
 
+// NVFP4 tiles are stored with the 16-byte pieces of row r swapped in pairs
+// when bit 3 of r is set (piece p at p ^ nv_swz(r)): 16 consecutive rows then
+// start in 16 different 16-byte bank groups (a 352-byte row stride alone
+// repeats them every 8 rows), for the score waves' 16-byte row reads and
+// the value waves' transposing reads alike.
+__device__ __forceinline__ int nv_swz(int r) { return (r >> 3) & 1; }
+
 __device__ __forceinline__ half8_t join(half2_t a, half2_t b, half2_t c, half2_t d) {
     half8_t r;
     r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
@@ -257,7 +264,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         const int r = min(slot / kChunks, kTile - 1);
         const int c = slot % kChunks;
         dma_row[k] = r;
-        dma_off[k] = 16 * ((kFp8 && c < kLatent / 16) ? (c ^ fp8_swz(r)) : c);
+        dma_off[k] = 16 * (kFp8 ? (c < kLatent / 16 ? (c ^ fp8_swz(r)) : c) : (c ^ nv_swz(r)));
     }
     const uint32_t ring_addr = (uint32_t)(size_t)(lds_void_t *)ring;
     // the row ids of this wave's loads of tile T, then the loads themselves
@@ -283,11 +290,6 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     auto read_flags = [&](int pb) {
         const uint4 f = *reinterpret_cast<const uint4 *>(&flag_lds[pb][0]);
         return f;
-    };
-    // the flags as a wave-uniform bit mask (bit w: score wave w flagged)
-    auto flag_mask = [&](const uint4 &f) -> uint32_t {
-        return __builtin_amdgcn_readfirstlane((f.x ? 1u : 0u) | (f.y ? 2u : 0u) | (f.z ? 4u : 0u) |
-                                              (f.w ? 8u : 0u));
     };
     // tile t is in LDS once at most the loads of the tiles issued after it
     // are outstanding: `after` of them (value waves only)
@@ -375,6 +377,13 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         int lat_off[8];
 #pragma unroll
         for (int jp = 0; jp < 8; ++jp) lat_off[jp] = 16 * (8 * g + (jp ^ fp8_swz(row)));
+        // NVFP4: the byte offsets of this lane's nibble pieces, scales and
+        // rope bytes within its row (pieces swapped by nv_swz(row))
+        int nib_off[4];
+#pragma unroll
+        for (int jp = 0; jp < 4; ++jp) nib_off[jp] = 16 * ((4 * g + jp) ^ nv_swz(row));
+        const int sc_off = 16 * ((kScaleOff / 16 + (g >> 1)) ^ nv_swz(row)) + 8 * (g & 1);
+        const int rope_off = 16 * ((kRopeOff / 16 + g) ^ nv_swz(row));
         auto load_packed = [&](int T, Packed &pk) {
             const uint8_t *rp = ring + (T % kNBuf) * kTileBytes + row * kRowB;
             if constexpr (kFp8) {
@@ -382,11 +391,10 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                 for (int jp = 0; jp < 8; ++jp) pk.lat[jp] = *reinterpret_cast<const uint4 *>(rp + lat_off[jp]);
             } else {
 #pragma unroll
-                for (int jp = 0; jp < 4; ++jp)
-                    pk.nib[jp] = *reinterpret_cast<const uint4 *>(rp + 16 * (4 * g + jp));
-                pk.sc = *reinterpret_cast<const uint2 *>(rp + kScaleOff + 8 * g);
+                for (int jp = 0; jp < 4; ++jp) pk.nib[jp] = *reinterpret_cast<const uint4 *>(rp + nib_off[jp]);
+                pk.sc = *reinterpret_cast<const uint2 *>(rp + sc_off);
             }
-            pk.rope = *reinterpret_cast<const uint4 *>(rp + R::kRopeAt + 16 * g);
+            pk.rope = *reinterpret_cast<const uint4 *>(rp + (kFp8 ? R::kRopeAt + 16 * g : rope_off));
         };
         // unpack and score: d = scale_log2 * q.k - m_run of this wave's 16
         // rows (-inf for rows past the end of the list); sp = the {S,S}
@@ -466,10 +474,10 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 
         for (int s = 0; s <= n_tiles + 1; ++s) {
             __syncthreads();                                            // B(s)
-            // the flags of tile s - 1 (written in step s - 1), read early so
-            // that the read completes under the scoring
-            uint4 fl = {0u, 0u, 0u, 0u};
-            if (s >= 1 && s - 1 < n_tiles) fl = read_flags((s - 1) & 1);
+            // the flags of tile s - 1 (written in step s - 1), read in every
+            // step (they mean something only when tile s - 1 exists) and used
+            // only after the scoring, so that the read completes under it
+            uint4 fl = read_flags((s + 1) & 1);
             // (a) scores of tile s from the bytes read during step s - 1,
             // relative to the running max
             float d[MB][4];
@@ -503,12 +511,16 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                 }
             }
             // (b) did tile s - 1 move the running max?  Then: new max from
-            // the waves' tile maxima (an unflagged wave published -inf, and
-            // its scores lie within kSlack of the old max); tile s - 1 is
+            // the flagged waves' tile maxima (an unflagged wave's scores lie
+            // within kSlack of the old max); tile s - 1 is
             // re-weighted from its kept d before S(s), and the d of tile s
             // are moved to the new max; the value waves rescale O and the
-            // sum after S(s)
-            if (s >= 1 && s - 1 < n_tiles && flag_mask(fl) != 0) {
+            // sum after S(s).  (The scheduling barrier and the empty asm keep
+            // the flags' first use, and so the wait for them, after the
+            // scoring.)
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" : "+v"(fl.x), "+v"(fl.y), "+v"(fl.z), "+v"(fl.w));
+            if (s >= 1 && s - 1 < n_tiles && __builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w) != 0) {
                 const int pb = (s - 1) & 1;
                 float shift[MB][4];
 #pragma unroll
@@ -516,8 +528,10 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int h = mb * 16 + 4 * g + r;
-                        const float mt = fmaxf(fmaxf(m_run[mb][r], fmaxf(red_lds[pb][0][h], red_lds[pb][1][h])),
-                                               fmaxf(red_lds[pb][2][h], red_lds[pb][3][h]));
+                        const float mt = fmaxf(fmaxf(m_run[mb][r], fmaxf(fl.x ? red_lds[pb][0][h] : -INFINITY,
+                                                                         fl.y ? red_lds[pb][1][h] : -INFINITY)),
+                                               fmaxf(fl.z ? red_lds[pb][2][h] : -INFINITY,
+                                                     fl.w ? red_lds[pb][3][h] : -INFINITY));
                         shift[mb][r] = m_run[mb][r] - mt;  // <= 0
                         if (sw == 0 && n == 0) alpha_lds[pb][h] = __builtin_amdgcn_exp2f(shift[mb][r]);
                         m_run[mb][r] = mt;
@@ -549,23 +563,20 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                 for (int r = 0; r < 4; ++r) over |= d[mb][r] > kSlack;
             const bool flagged = __ballot(over) != 0;
             if (lane == 0) flag_lds[pb][sw] = flagged;
-            // this wave's tile maxima per head (-inf when it did not flag)
-            float mx[MB][4];
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) mx[mb][r] = -INFINITY;
+            // this wave's tile maxima per head, published only when it flagged
+            // (the re-weight takes the maxima of the flagged waves only)
             if (flagged) {
+                float mx[MB][4];
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) mx[mb][r] = row16_max(d[mb][r]) + m_run[mb][r];
-            }
-            if (n == 0) {
+                if (n == 0) {
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    *reinterpret_cast<float4_t *>(&red_lds[pb][sw][mb * 16 + 4 * g]) =
-                        float4_t{mx[mb][0], mx[mb][1], mx[mb][2], mx[mb][3]};
+                    for (int mb = 0; mb < MB; ++mb)
+                        *reinterpret_cast<float4_t *>(&red_lds[pb][sw][mb * 16 + 4 * g]) =
+                            float4_t{mx[mb][0], mx[mb][1], mx[mb][2], mx[mb][3]};
+                }
             }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -706,13 +717,15 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                         (__attribute__((address_space(3))) const uint8_t *)(vb + (32 * rb + 8 * t) * kRowB)));
             }
         } else {
-            const uint8_t *vb = tb + v_lane;
+            // piece 4 sw + cb of the lane's row sits at 4 sw + (cb ^ nv_swz(row))
+            const uint8_t *vb0 = tb + v_lane + 16 * nv_swz(lane & 15);
+            const uint8_t *vb1 = tb + v_lane + 16 * (1 - nv_swz(lane & 15));
             const uint8_t *sb = reinterpret_cast<const uint8_t *>(st_lds[pb]) + s_lane;
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
                 // columns 128 sw + 32 cb + n32: packed bytes 16 cb further, block 2 cb further
                 vv[cb][rb] = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_int2_t *)(
-                    (__attribute__((address_space(3))) const uint8_t *)(vb + 32 * rb * kRowB + 16 * cb)));
+                    (__attribute__((address_space(3))) const uint8_t *)((cb & 1 ? vb1 : vb0) + 32 * rb * kRowB + 32 * (cb >> 1))));
                 const half8_t *sp8 = reinterpret_cast<const half8_t *>(sb + (2 * cb * kSStride + 32 * rb) * 2);
                 sv[cb][rb][0] = sp8[0];
                 sv[cb][rb][1] = sp8[1];
@@ -762,10 +775,10 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         asm volatile("" : "+v"(ones));  // kept in registers, not rebuilt per use
         // step s contracts tile s - 2 (operands in registers) and reads the
         // operands of tile s - 1; the flags of tile s - 1 say whether the
-        // score waves re-weight it before S(s)
+        // score waves re-weight it before S(s) (read in every step, used
+        // at its end)
         const bool cur = s >= 1 && s - 1 < n_tiles;
-        uint4 fl = {0u, 0u, 0u, 0u};
-        if (cur) fl = read_flags((s - 1) & 1);
+        const uint4 fl = read_flags((s + 1) & 1);
         if (s == 0) {
             // tile 1 (read by the score waves after F0) is complete before F0
             if (1 < n_tiles) wait_tile(min(kAhead - 2, n_tiles - 2));
@@ -818,7 +831,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         }
         if (kFp8 && s == n_tiles && (n_valid & (kTile - 1)) != 0) mask_padding(n_valid & (kTile - 1));
         if (s + kAhead + 1 < n_tiles) tile_rows(s + kAhead + 1, rk);
-        if (cur && flag_mask(fl) != 0) {
+        if (cur && __builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w) != 0) {
             // tile s - 1 moved the running max: the score waves re-weight
             // it before S(s); O and the sum (tiles up to s - 2) are rescaled
             __syncthreads();                                            // S(s)
