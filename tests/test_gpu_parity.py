@@ -444,3 +444,30 @@ def test_decode_max_batch(dev, smla):
         assert e_out <= OUT_TOL and e_lse <= LSE_TOL
     del rows, q, out, lse, cache
     torch.cuda.empty_cache()
+
+
+def test_decode_workspace_reuse_across_shapes(dev, smla):
+    """One workspace serves calls of different shapes and both row formats
+    in a row: each result equals the one a fresh workspace gives (bit for
+    bit: the merge order is fixed)."""
+    note("decode workspace reuse across shapes")
+    from cases import gpu_cache, small_case
+    shapes = [(2, 64, [5000, 1500], 2048), (1, 16, [4096], 256), (4, 16, [2500, 2500, 90, 700], 2048),
+              (5, 64, [2100, 300, 64, 1, 4000], 2048), (1, 64, [70000], 2048), (3, 16, [3000, 777, 64], 512)]
+    need = max(max(smla.decode_workspace_bytes(b, h, k), smla.decode_workspace_bytes_fp8(b, h, k))
+               for b, h, _, k in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    for trial, (batch, heads, lens, topk) in enumerate(shapes * 2):
+        case = small_case(batch, heads, lens, topk, seed=300 + trial)
+        fp8 = trial % 3 == 2
+        cache_d = gpu_cache(case, dev, smla, fmt="fp8" if fp8 else "nvfp4")
+        fn, wsb = ((smla.sparse_mla_decode_fp8, smla.decode_workspace_bytes_fp8) if fp8
+                   else (smla.sparse_mla_decode, smla.decode_workspace_bytes))
+        args = (to_dev_bf16(case["q"], dev), cache_d, torch.as_tensor(case["pt"], device=dev),
+                torch.as_tensor(case["lens"].astype(np.int32), device=dev),
+                torch.as_tensor(case["topk"], device=dev), case["scale"])
+        o1, l1 = fn(*args, workspace=ws)
+        fresh = torch.full((max(wsb(batch, heads, topk), 256),), 0x5A, dtype=torch.uint8, device=dev)
+        o2, l2 = fn(*args, workspace=fresh)
+        torch.cuda.synchronize(dev)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), trial
