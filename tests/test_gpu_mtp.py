@@ -61,6 +61,8 @@ MTP_CASES = [
     (1, 3, 16, [70000], 2048),
     (5, 2, 64, [64, 65, 129, 2, 4000], 64),
     (4, 4, 16, [2500, 2500, 90, 700], 2048),
+    (2, 16, 64, [3000, 40], 1024),    # the most tokens a call takes
+    (1, 16, 16, [10], 256),           # fewer positions than tokens: early tokens see none
 ]
 
 
