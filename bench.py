@@ -147,6 +147,21 @@ def summarize_counters(fetch_dir, write_dir, workload):
     return "\n".join(lines)
 
 
+def events_ms(fn, n):
+    """Mean milliseconds per call of fn(0 .. n-1), from two HIP events on the
+    current stream (the stream the library launches on) around the n calls,
+    with a synchronisation before and after."""
+    import torch
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def summarize_pmc(dirs):
     """Per-kernel averages per dispatch of the counters in one or more
     rocprofv3 --pmc directories, and what they imply.  GRBM_GUI_ACTIVE as
@@ -314,27 +329,21 @@ def bench_mtp(args, w, dev):
                      dtype=torch.uint8, device=dev)
     log("mtp %s T=%d: %d sets, %d rows appended per step" % (w.name, T, sets, rows.shape[0]))
 
-    def step(i, ev=None):
+    def decode_call(i):
         st = i % sets
-        if ev is not None:
-            ev[0].record()
-        smla.kv_quant_append(rows, slots, cache)
-        if ev is not None:
-            ev[1].record()
         smla.sparse_mla_decode_mtp(qs[st], cache, pt, sl, tks[st], w.softmax_scale, out=out,
                                    lse=lse, workspace=ws)
-        if ev is not None:
-            ev[2].record()
+
+    def step(i):
+        smla.kv_quant_append(rows, slots, cache)
+        decode_call(i)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
+    events_ms(lambda i: step(args.warmup + i), args.steps)
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    dec_s = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    dec_s = events_ms(lambda i: decode_call(args.warmup + i), args.steps) * 1e-3
     used = [(args.warmup + i) % sets for i in range(args.steps)]
     dec_bytes = float(np.mean([nvalid[u] for u in used])) * 352
     uniq_bytes = float(np.mean([nuniq[u] for u in used])) * 352
@@ -514,31 +523,29 @@ def main():
             smla.sparse_mla_decode_fp8(q_, staged, spt, ssl, staged_topk, scale_, out=out,
                                        lse=lse, workspace=workspace)
 
-    def step(i, ev=None):
+    def decode_call(i):
         s = i % sets
-        if ev is not None:
-            ev[0].record()
-        append_fn(step_rows, step_slots, cache)
-        if ev is not None:
-            ev[1].record()
         decode_fn(qs[s], cache, pt, sl, tks[s], w.softmax_scale, out=out, lse=lse, workspace=ws)
-        if ev is not None:
-            ev[2].record()
+
+    def step(i):
+        append_fn(step_rows, step_slots, cache)
+        decode_call(i)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # the timed steps: wall clock between two synchronisations, and two HIP
+    # events on the library's stream around them (nothing is recorded between
+    # the steps: an event record inside the loop costs the step ~8 us)
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
+    gpu_step_ms = events_ms(lambda i: step(args.warmup + i), args.steps)
     t_total = time.perf_counter() - t_start
-    app_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     ms_per_step = t_total * 1e3 / args.steps
+    # the decode call and the append alone, each timed the same way over as
+    # many back-to-back calls with the same inputs
+    dec_ms = np.array([events_ms(lambda i: decode_call(args.warmup + i), args.steps)])
+    app_ms = np.array([events_ms(lambda i: append_fn(step_rows, step_slots, cache), args.steps)])
 
     # algorithmic work per step (mean over the sets the timed steps used)
     used = [(args.warmup + i) % sets for i in range(args.steps)]
@@ -586,6 +593,7 @@ def main():
         "decode_kv_GBps": round(dec_gbps, 1),
         "decode_tflops": round(dec_tflops, 2),
         "append_us": round(float(app_ms.mean()) * 1e3, 2),
+        "gpu_us_per_step": round(gpu_step_ms * 1e3, 2),
         "roofline": roof,
     }
     if not args.no_cpu:
