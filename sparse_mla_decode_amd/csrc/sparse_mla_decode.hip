@@ -908,11 +908,14 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 // Merge of the splits' partials: one wave per (unit, head), a lane per 8
 // columns; the wave of a head of sequence sq runs on XCD sq % 8, where the
 // decode workgroups of sq wrote the partials (so they are read from that L2).
-// The (m, l) pairs are wave-uniform (scalar loads), every split's loads are
-// issued up front, then combined in split order (fixed, hence
-// deterministic):
+// kS is the split count rounded up to 2, 4, 8 or 16.  Every load is issued
+// before any is used (one round trip): each split's 16 bytes of the lane's
+// columns, and, in lane s, the (m, l) of split s, which every lane then
+// takes by readlane.  Splits past the count re-read the last one and get
+// weight 0.  They are combined in split order (fixed, hence deterministic):
 //   M = max_s m_s,  w_s = 2^(m_s - M) l_s,  out = sum_s w_s O_s / sum_s w_s,
 //   lse = ln 2 * (M + log2 sum_s w_s).
+template <int kS>
 __global__ __launch_bounds__(256) void merge_splits_kernel(
     const _Float16 *__restrict__ part_o, const float *__restrict__ part_ml,
     float *__restrict__ out, float *__restrict__ lse, int32_t heads, int32_t hg_size,
@@ -927,34 +930,31 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(
     const int lane = threadIdx.x & 63;
     const int h = p % hg_size;
     const int unit = b * groups + (p % per_seq) / hg_size;
-    float ms[kMaxSplits], ls[kMaxSplits];
-    half8_t os[kMaxSplits];
+    half8_t os[kS];
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-        if (s < splits) {
-            const size_t pidx = ((size_t)unit * splits + s) * hg_size + h;
-            ms[s] = part_ml[pidx * 2];
-            ls[s] = part_ml[pidx * 2 + 1];
-            os[s] = *reinterpret_cast<const half8_t *>(part_o + pidx * kLatent + 8 * lane);
-        } else {
-            ms[s] = -INFINITY;
-            ls[s] = 0.f;
-            os[s] = half8_t{};
-        }
+    for (int s = 0; s < kS; ++s) {
+        const size_t pidx = ((size_t)unit * splits + min(s, splits - 1)) * hg_size + h;
+        os[s] = *reinterpret_cast<const half8_t *>(part_o + pidx * kLatent + 8 * lane);
     }
+    const float *mlp = part_ml + (((size_t)unit * splits + min(lane, splits - 1)) * hg_size + h) * 2;
+    const int mv = __builtin_bit_cast(int, mlp[0]), lv = __builtin_bit_cast(int, mlp[1]);
+    float2_t ml[kS];
+#pragma unroll
+    for (int s = 0; s < kS; ++s)
+        ml[s] = float2_t{__builtin_bit_cast(float, __builtin_amdgcn_readlane(mv, s)),
+                         __builtin_bit_cast(float, __builtin_amdgcn_readlane(lv, s))};
     float M = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, ls[s] > 0.f ? ms[s] : -INFINITY);
+    for (int s = 0; s < kS; ++s) M = fmaxf(M, (s < splits && ml[s][1] > 0.f) ? ml[s][0] : -INFINITY);
+    const float Ms = M == -INFINITY ? 0.f : M;  // no usable split: every weight is 0
     float L = 0.f;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
 #pragma unroll
-        for (int s = 0; s < kMaxSplits; ++s) {
-            const float w = ls[s] > 0.f ? __builtin_amdgcn_exp2f(ms[s] - M) * ls[s] : 0.f;
-            L += w;
+    for (int s = 0; s < kS; ++s) {
+        const float w = (s < splits && ml[s][1] > 0.f) ? __builtin_amdgcn_exp2f(ml[s][0] - Ms) * ml[s][1] : 0.f;
+        L += w;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) acc[k] += w * (float)os[s][k];
-        }
+        for (int k = 0; k < 8; ++k) acc[k] += w * (float)os[s][k];
     }
     const int head = (unit % groups) * hg_size + h;
     const float inv = L > 0.f ? 1.0f / L : 0.f;
@@ -1033,9 +1033,15 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
     // one wave per (unit, head); the blocks of XCD x take the sequences sq = x mod 8
     const int64_t per_xcd =
         (int64_t)((batch + 7) / 8) * tokens * plan.groups * plan.heads_per_group;
-    hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)(8 * ((per_xcd + 3) / 4))), dim3(256), 0,
-                       stream, part_o, part_ml, out, lse, heads, plan.heads_per_group,
-                       plan.groups, plan.splits, batch, tokens);
+    const dim3 mg((unsigned)(8 * ((per_xcd + 3) / 4)));
+#define SMLA_MERGE(S) hipLaunchKernelGGL((merge_splits_kernel<S>), mg, dim3(256), 0, stream, part_o, part_ml, \
+                                         out, lse, heads, plan.heads_per_group, plan.groups, plan.splits, \
+                                         batch, tokens)
+    if (plan.splits <= 2) SMLA_MERGE(2);
+    else if (plan.splits <= 4) SMLA_MERGE(4);
+    else if (plan.splits <= 8) SMLA_MERGE(8);
+    else SMLA_MERGE(16);
+#undef SMLA_MERGE
     return hipGetLastError();
 }
 
