@@ -129,19 +129,28 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(
     for (int i = tid; i < kBins0; i += kThreads) h[i] = 0u;
     __syncthreads();
     const float *row = scores + b * ld;
+    // every load in flight before any is used
+    float4 v[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int64_t i0 = begin + 4 * (int64_t)(tid + kThreads * k);
-        if (i0 >= L) break;
-        const float4 v = *reinterpret_cast<const float4 *>(row + i0);
-        const float x[4] = {v.x, v.y, v.z, v.w};
+        v[k] = *reinterpret_cast<const float4 *>(row + min(i0, ld - 4));  // in the row; masked below
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int64_t i0 = begin + 4 * (int64_t)(tid + kThreads * k);
+        const float x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             if (i0 + j < L) atomicAdd(&h[score_key(x[j]) >> 21], 1u);
     }
     __syncthreads();
-    for (int i = tid; i < kBins0; i += kThreads)
-        if (h[i]) atomicAdd(&q[kHist0 + i], h[i]);
+    uint32_t hv[kBins0 / kThreads];
+#pragma unroll
+    for (int k = 0; k < kBins0 / kThreads; ++k) hv[k] = h[tid + kThreads * k];
+#pragma unroll
+    for (int k = 0; k < kBins0 / kThreads; ++k)
+        if (hv[k]) atomicAdd(&q[kHist0 + tid + kThreads * k], hv[k]);
 }
 
 // Pass 1: keys above bin b0 to the list, keys in b0 to the candidates.
@@ -160,6 +169,13 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(
     const int64_t begin = (int64_t)c * kChunk;
     if (begin >= L) return;
     uint32_t *q = ws + b * ws_stride;
+    const float *row = scores + b * ld;
+    float4 v[kPer];  // the chunk's loads in flight while the threshold bin is found
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int64_t i0 = begin + 4 * (int64_t)(tid + kThreads * k);
+        v[k] = *reinterpret_cast<const float4 *>(row + min(i0, ld - 4));  // in the row; masked below
+    }
     uint32_t b0, a0;
     find_bin<kBins0, kThreads>(q + kHist0, (uint32_t)topk, scan_lds, res_lds, b0, a0);
     if (c == 0 && tid == 0) {
@@ -167,17 +183,12 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(
         q[kState + 1] = a0;
     }
     a0 = min(a0, (uint32_t)topk - 1);  // keeps every store inside the list
-    const float *row = scores + b * ld;
     uint32_t gt_mask = 0, in_mask = 0;  // bit 4k + j: score i0(k) + j
     uint32_t keys[4 * kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int64_t i0 = begin + 4 * (int64_t)(tid + kThreads * k);
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
-        if (i0 < L) {
-            const float4 v = *reinterpret_cast<const float4 *>(row + i0);
-            x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-        }
+        const float x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t key = score_key(x[j]);
