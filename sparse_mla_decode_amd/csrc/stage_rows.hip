@@ -17,11 +17,10 @@
 //
 // Mapping: a 256-thread workgroup stages 64 consecutive entries of one
 // sequence.  The first 64 threads validate and translate the entries (one
-// index load, one page-table load each) into LDS; then the 64 x 36 16-byte
-// pieces of the copy (pieces 0..31 of a row are its latent blocks -- 8 nibble
-// bytes and one scale each -- and 32..35 its rope bytes) are dealt to the
-// threads in order, 9 each, so the copy is written as one contiguous stream
-// and every thread has all its row loads in flight at once.  The decoded
+// index load, one page-table load each) into LDS; then every thread takes 8
+// of the 64 x 32 latent blocks (8 nibble bytes and one scale each, one
+// 16-byte piece of the copy) and one of the 64 x 4 rope pieces, with all its
+// row loads in flight at once.  The decoded
 // values (e2m1 x S, exact in fp32) are clamped to [-448, 448] and converted
 // by the hardware's round-to-nearest-even FP8 conversion, which is then the
 // nearest-E4M3 rule with saturation.
@@ -33,7 +32,6 @@ namespace {
 
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kPieces = kFp8RowBytes / 16;  // 36
 
 // e2m1 pair (byte SEL of w, low nibble first) -> two floats, exact
 template <int SEL>
@@ -67,35 +65,30 @@ __global__ __launch_bounds__(256) void stage_rows_fp8_kernel(
     }
     __syncthreads();
     uint8_t *out_base = staged + (b * kpad + e0) * kFp8RowBytes;
-    uint2 nib[9];
-    uint4 rope[9];
-    uint32_t sc[9];
-    bool use[9];
+    // Loads first, all of them unconditional (an unusable entry reads row 0
+    // of page 0, which every cache has, and is skipped below), so that none
+    // waits for another: the 8 latent pieces of this thread (piece p = tid +
+    // 256 k is block p % 32 of row p / 32: 8 nibble bytes and a scale byte)
+    // and its one rope piece (the 16 bytes 16 (tid % 4) .. of row tid / 4).
+    uint2 nib[8];
+    uint32_t sc[8];
 #pragma unroll
-    for (int k = 0; k < 9; ++k) {
-        const int p = tid + 256 * k;  // piece of the 64-row block
-        const int rl = p / kPieces, j = p - rl * kPieces;
-        const int64_t r = row_lds[rl];
-        use[k] = r >= 0;
-        const uint8_t *row = cache + (use[k] ? r : 0) * kRowBytes;
-        if (j < 32) {
-            nib[k] = use[k] ? *reinterpret_cast<const uint2 *>(row + 8 * j) : make_uint2(0u, 0u);
-            sc[k] = use[k] ? row[kScaleOff + j] : 0u;
-        } else {
-            rope[k] = use[k] ? *reinterpret_cast<const uint4 *>(row + kRopeOff + 16 * (j - 32))
-                             : make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
+    for (int k = 0; k < 8; ++k) {
         const int p = tid + 256 * k;
-        const int rl = p / kPieces, j = p - rl * kPieces;
-        if (!use[k]) continue;
+        const int64_t r = max(row_lds[p >> 5], (int64_t)0);
+        const uint8_t *row = cache + r * kRowBytes;
+        nib[k] = *reinterpret_cast<const uint2 *>(row + 8 * (p & 31));
+        sc[k] = row[kScaleOff + (p & 31)];
+    }
+    const int64_t rr = row_lds[tid >> 2];
+    const uint4 rope = *reinterpret_cast<const uint4 *>(cache + max(rr, (int64_t)0) * kRowBytes + kRopeOff +
+                                                        16 * (tid & 3));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int p = tid + 256 * k;
+        const int rl = p >> 5, j = p & 31;
+        if (row_lds[rl] < 0) continue;
         uint4 *dst = reinterpret_cast<uint4 *>(out_base + (int64_t)rl * kFp8RowBytes) + j;
-        if (j >= 32) {
-            *dst = rope[k];
-            continue;
-        }
         const float S = (sc[k] & 0x80u) ? -e4m3_mag(sc[k]) : e4m3_mag(sc[k]);
         const uint32_t w[2] = {nib[k].x, nib[k].y};
         uint32_t o[4];
@@ -115,6 +108,8 @@ __global__ __launch_bounds__(256) void stage_rows_fp8_kernel(
         }
         *dst = make_uint4(o[0], o[1], o[2], o[3]);
     }
+    if (rr >= 0)
+        *(reinterpret_cast<uint4 *>(out_base + (int64_t)(tid >> 2) * kFp8RowBytes + kLatent) + (tid & 3)) = rope;
 }
 
 }  // namespace
