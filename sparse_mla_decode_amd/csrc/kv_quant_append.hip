@@ -68,14 +68,18 @@ __global__ __launch_bounds__(256) void kv_quant_append_kernel(const uint16_t *__
     const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
     const int j = threadIdx.x & 31;
     if (row >= n) return;
-    const int64_t slot = slots[row];
-    if (slot < 0 || slot >= num_slots) return;
+    // the row's loads and the slot's in flight together; the slot decides
+    // only the store
     const uint16_t *x = rows + row * kDim;
-    uint8_t *dst = cache + slot * kRowBytes;
-
-    // ---- latent block j ----
     const uint4 lo = *reinterpret_cast<const uint4 *>(x + j * kBlock);
     const uint4 hi = *reinterpret_cast<const uint4 *>(x + j * kBlock + 8);
+    const uint32_t r = *reinterpret_cast<const uint32_t *>(x + kLatent + 2 * j);
+    const int64_t slot = slots[row];
+    // (no early return on the slot: the loads would then wait for it)
+    const bool ok = slot >= 0 && slot < num_slots;
+    uint8_t *dst = cache + (ok ? slot : 0) * kRowBytes;
+
+    // ---- latent block j ----
     uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     uint32_t amax_bits = 0;
 #pragma unroll
@@ -95,11 +99,11 @@ __global__ __launch_bounds__(256) void kv_quant_append_kernel(const uint16_t *__
         const uint32_t nib = mag | ((h >> 12) & 8u);
         packed[i >> 3] |= nib << ((i & 7) * 4);
     }
+    if (!ok) return;
     *reinterpret_cast<uint2 *>(dst + j * 8) = make_uint2(packed[0], packed[1]);
     dst[kScaleOff + j] = (uint8_t)s;
 
     // ---- rope values 2j, 2j+1 ----
-    const uint32_t r = *reinterpret_cast<const uint32_t *>(x + kLatent + 2 * j);
     const uint32_t c0 = e4m3_nearest(__uint_as_float((r & 0xFFFFu) << 16));
     const uint32_t c1 = e4m3_nearest(__uint_as_float(r & 0xFFFF0000u));
     *reinterpret_cast<uint16_t *>(dst + kRopeOff + 2 * j) = (uint16_t)(c0 | (c1 << 8));
@@ -113,10 +117,9 @@ __global__ __launch_bounds__(288) void kv_quant_append_fp8_kernel(const uint16_t
     const int64_t row = (int64_t)blockIdx.x * 8 + threadIdx.x / 36;
     const int j = threadIdx.x % 36;
     if (row >= n) return;
-    const int64_t slot = slots[row];
-    if (slot < 0 || slot >= num_slots) return;
     const uint4 lo = *reinterpret_cast<const uint4 *>(rows + row * kDim + 16 * j);
     const uint4 hi = *reinterpret_cast<const uint4 *>(rows + row * kDim + 16 * j + 8);
+    const int64_t slot = slots[row];
     const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     uint32_t b[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -125,6 +128,7 @@ __global__ __launch_bounds__(288) void kv_quant_append_fp8_kernel(const uint16_t
         const uint32_t c1 = e4m3_nearest(__uint_as_float(w[i] & 0xFFFF0000u));
         b[i >> 1] |= (c0 | (c1 << 8)) << (16 * (i & 1));
     }
+    if (slot < 0 || slot >= num_slots) return;
     *reinterpret_cast<uint4 *>(cache + slot * kFp8RowBytes + 16 * j) = make_uint4(b[0], b[1], b[2], b[3]);
 }
 
