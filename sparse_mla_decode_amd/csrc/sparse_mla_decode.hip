@@ -281,6 +281,14 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
             if (k < n_dma)
                 dma16(cache + (size_t)rk[k] * kRowB + dma_off[k], dst + (uint32_t)(k * 4 * 1024));
     };
+    // loads k0 .. k1 - 1 of this wave's share of tile T
+    auto tile_dma_part = [&](int T, const uint32_t (&rk)[kMaxDma], int k0, int k1) {
+        const uint32_t dst = ring_addr + (uint32_t)((T % kNBuf) * kTileBytes + sw * 1024);
+#pragma unroll
+        for (int k = 0; k < kMaxDma; ++k)
+            if (k >= k0 && k < k1 && k < n_dma)
+                dma16(cache + (size_t)rk[k] * kRowB + dma_off[k], dst + (uint32_t)(k * 4 * 1024));
+    };
     auto issue = [&](int T) {
         uint32_t rk[kMaxDma];
         tile_rows(T, rk);
@@ -755,15 +763,17 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         }
     };
 
-    // tiles 0 and 1 first (tile 2 follows once tile 0 is in, so that tile 0
-    // and the query are not queued behind it), then wait until tile 0 is in
-    // LDS.
+    // tiles 0 and 1 first, then wait until tile 0 is in LDS; tile 2 follows
+    // in step 0, after B(0).  A wave's direct-to-LDS load waits at issue
+    // while too many of the CU's are outstanding: issued here, tile 2's
+    // loads would hold the value waves (and through B(0) the score waves)
+    // until tile 1's had drained; after B(0) that wait overlaps the scoring
+    // of tile 0.
     // Tile t + 1 is complete one barrier before the score waves read it at
     // the end of step t: before F0 for t = 0, before B(t) after that
     for (int T = 0; T <= 1 && T < n_tiles; ++T) issue(T);
     if (n_tiles > 0) wait_tile(min(1, n_tiles - 1));
     __syncthreads();
-    for (int T = 2; T < kAhead && T < n_tiles; ++T) issue(T);
     uint32_t rk[kMaxDma];  // row ids of the next tile to load
     if (kAhead < n_tiles) tile_rows(kAhead, rk);
 
@@ -780,14 +790,18 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         const bool cur = s >= 1 && s - 1 < n_tiles;
         const uint4 fl = read_flags((s + 1) & 1);
         if (s == 0) {
+            for (int T = 2; T < kAhead && T < n_tiles; ++T) issue(T);
             // tile 1 (read by the score waves after F0) is complete before F0
             if (1 < n_tiles) wait_tile(min(kAhead - 2, n_tiles - 2));
             __syncthreads();                                            // F0
         }
         // tile s + kAhead into the slot of tile s - 2 (read for the last time
-        // in step s - 1), as early as possible; its row ids were read in step
-        // s - 1
-        if (s + kAhead < n_tiles) tile_dma(s + kAhead, rk);
+        // in step s - 1); its row ids were read in step s - 1.  From step 2
+        // on the loads are spread over the contraction, a quarter after each
+        // row group, so that their waits at issue (see above) fall under the
+        // matrix instructions
+        const bool dma_now = s + kAhead < n_tiles;
+        if (dma_now && s < 2) tile_dma(s + kAhead, rk);
         // the weights of tile s - 1 (A operands); read again after S(s)
         // when the score waves re-weight that tile
         const int pb = (s - 1) & 1;
@@ -822,6 +836,10 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                 if (rt == sw) lacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[rt], ones, lacc, 0, 0, 0);
                 read_weights(rt);
                 if (t == 1) read_values(s, rb);
+                if (dma_now) {
+                    constexpr int kPer = (kMaxDma + 3) / 4;  // loads per row group (2 or 3)
+                    tile_dma_part(s + kAhead, rk, kPer * rt, kPer * rt + kPer);
+                }
             }
         } else {
             read_values(s, 0);
