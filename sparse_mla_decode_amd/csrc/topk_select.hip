@@ -10,8 +10,9 @@
 // Radix select over an order-preserving 32-bit key of each fp32 score, in
 // three digits (bits 31..21, 20..10, 9..0).  Two passes read every score:
 //   pass 0: histogram of digit 0 over the query's L scores (workgroups of
-//           4096 scores: LDS histogram, then the non-empty bins added to the
-//           query's histogram with global atomics);
+//           4096 scores, 8192 for long rows: LDS histogram, then the
+//           non-empty bins added to the query's histogram with global
+//           atomics);
 //   pass 1: every workgroup finds, from that histogram, the bin b0 holding
 //           the K-th largest key and the count a0 of keys above it; keys
 //           above b0 go straight to the list (one atomic per workgroup
@@ -36,9 +37,11 @@
 namespace smla {
 namespace {
 
-constexpr int kChunk = 4096;          // scores per workgroup of the full passes
-constexpr int kThreads = 256;
-constexpr int kPer = kChunk / (4 * kThreads);  // float4 loads per thread (4)
+// Scores per workgroup of the two full passes, and its threads: 4096 and
+// 256, or, for rows of 256K scores or more, 8192 and 512 (fewer workgroups
+// adding into each query's histogram).  Every thread loads 4 float4.
+constexpr int kPer = 4;
+constexpr int64_t kBigRow = 262144;
 constexpr int kFinThreads = 1024;
 constexpr int kBins0 = 2048, kBins1 = 2048, kBins2 = 1024;
 constexpr int kHist0 = 0;
@@ -114,6 +117,7 @@ __device__ void find_bin(const uint32_t *hist, uint32_t k, uint32_t *scan_lds, u
 }
 
 // Pass 0: histogram of digit 0.
+template <int kThreads>
 __global__ __launch_bounds__(kThreads) void topk_hist_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ seq_lens,
     int32_t topk, int32_t chunks, uint32_t *__restrict__ ws, int64_t ws_stride) {
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(
     const int tid = threadIdx.x;
     const int64_t L = min((int64_t)max(seq_lens[b], 0), ld);
     if (L <= topk) return;  // every position is selected: the finish alone
-    const int64_t begin = (int64_t)c * kChunk;
+    const int64_t begin = (int64_t)c * (4 * kPer * kThreads);
     if (begin >= L) return;  // chunk 0 always passes
     uint32_t *q = ws + b * ws_stride;
     for (int i = tid; i < kBins0; i += kThreads) h[i] = 0u;
@@ -154,6 +158,7 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(
 }
 
 // Pass 1: keys above bin b0 to the list, keys in b0 to the candidates.
+template <int kThreads>
 __global__ __launch_bounds__(kThreads) void topk_split_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ seq_lens,
     int32_t topk, int32_t chunks, uint32_t *__restrict__ ws, int64_t ws_stride, int64_t cap,
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(
     const int tid = threadIdx.x;
     const int64_t L = min((int64_t)max(seq_lens[b], 0), ld);
     if (L <= topk) return;
-    const int64_t begin = (int64_t)c * kChunk;
+    const int64_t begin = (int64_t)c * (4 * kPer * kThreads);
     if (begin >= L) return;
     uint32_t *q = ws + b * ws_stride;
     const float *row = scores + b * ld;
@@ -340,14 +345,21 @@ int64_t topk_workspace_stride(int64_t ld) {
 hipError_t launch_topk_select(const float *scores, int64_t ld, const int32_t *seq_lens,
                               int32_t batch, int32_t topk, int32_t *out, uint32_t *ws,
                               hipStream_t stream) {
-    const int32_t chunks = (int32_t)((ld + kChunk - 1) / kChunk);
-    const dim3 grid((unsigned)((int64_t)batch * chunks)), block(kThreads);
     const int64_t stride = topk_workspace_stride(ld);
     const int64_t cap = topk_candidate_cap(ld);
-    hipLaunchKernelGGL(topk_hist_kernel, grid, block, 0, stream, scores, ld, seq_lens, topk,
-                       chunks, ws, stride);
-    hipLaunchKernelGGL(topk_split_kernel, grid, block, 0, stream, scores, ld, seq_lens, topk,
-                       chunks, ws, stride, cap, out);
+#define SMLA_PASSES(NT)                                                                        \
+    do {                                                                                       \
+        const int64_t ch = 4 * kPer * (NT);                                                    \
+        const int32_t chunks = (int32_t)((ld + ch - 1) / ch);                                  \
+        const dim3 grid((unsigned)((int64_t)batch * chunks)), block(NT);                       \
+        hipLaunchKernelGGL(topk_hist_kernel<NT>, grid, block, 0, stream, scores, ld, seq_lens,  \
+                           topk, chunks, ws, stride);                                          \
+        hipLaunchKernelGGL(topk_split_kernel<NT>, grid, block, 0, stream, scores, ld, seq_lens, \
+                           topk, chunks, ws, stride, cap, out);                                \
+    } while (0)
+    if (ld >= kBigRow) SMLA_PASSES(512);
+    else SMLA_PASSES(256);
+#undef SMLA_PASSES
     hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)batch), dim3(kFinThreads), 0, stream,
                        scores, ld, seq_lens, topk, ws, stride, cap, out);
     return hipGetLastError();

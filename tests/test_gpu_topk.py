@@ -54,11 +54,11 @@ def run(smla, dev, scores: np.ndarray, lens: np.ndarray, K: int):
     return out.cpu().numpy()
 
 
-def test_select_random_rows_and_lengths(dev, smla):
-    note("topk random rows")
+@pytest.mark.parametrize("ld", [20000, 300000])  # the second takes the 8192-score workgroups
+def test_select_random_rows_and_lengths(dev, smla, ld):
+    note("topk random rows ld=%d" % ld)
     rng = np.random.default_rng(1)
-    ld = 20000
-    lens = np.array([20000, 2049, 2048, 2047, 1, 0, 4097, 19999, 13, 8192], dtype=np.int64)
+    lens = np.array([ld, 2049, 2048, 2047, 1, 0, 4097, ld - 1, 13, 8192], dtype=np.int64)
     x = rng.standard_normal((lens.size, ld)).astype(np.float32)
     got = run(smla, dev, x, lens, 2048)
     check_lists(got, x, lens, 2048, exact_sets=True)
