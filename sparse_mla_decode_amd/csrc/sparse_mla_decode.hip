@@ -53,6 +53,7 @@ namespace smla {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
@@ -900,10 +901,13 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         return;
     }
     // split: the normalised partial (f16) and its (m, l) for the merge
-    // kernel.  Layout: part_o [unit][split][HG][512], part_ml
-    // [unit][split][HG][2] = (running max in log2 units, sum).  The partials
-    // are streamed past the L2 (non-temporal stores), which leaves the L2 to
-    // the rows still being gathered.
+    // kernel.  Layout: part_o [unit][split][HG][4 sw][32 n32][4 cb] -- a
+    // head's 512 values in the order the value waves hold them, so that a
+    // lane writes its four column blocks as one 8-byte store (column
+    // 128 sw + 32 cb + n32) -- and part_ml [unit][split][HG][2] = (running
+    // max in log2 units, sum).  The partials are streamed past the L2
+    // (non-temporal stores), which leaves the L2 to the rows still being
+    // gathered.
     const size_t pidx = (size_t)unit * splits + split;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -911,10 +915,10 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         if (h >= HG) continue;
         const float l_tot = sum_lds[0][h] + sum_lds[1][h] + sum_lds[2][h] + sum_lds[3][h];
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-        _Float16 *prow = part_o + (pidx * HG + h) * kLatent + 128 * sw + n32;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-            __builtin_nontemporal_store((_Float16)(o[cb][i] * inv), &prow[32 * cb]);
+        const half4_t x4 = {(_Float16)(o[0][i] * inv), (_Float16)(o[1][i] * inv), (_Float16)(o[2][i] * inv),
+                            (_Float16)(o[3][i] * inv)};
+        __builtin_nontemporal_store(__builtin_bit_cast(uint64_t, x4),
+                                    reinterpret_cast<uint64_t *>(part_o) + (pidx * HG + h) * 128 + sw * 32 + n32);
     }
     if (vt < HG) {
         const float l_tot = sum_lds[0][vt] + sum_lds[1][vt] + sum_lds[2][vt] + sum_lds[3][vt];
@@ -923,8 +927,9 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     }
 }
 
-// Merge of the splits' partials: one wave per (unit, head), a lane per 8
-// columns; the wave of a head of sequence sq runs on XCD sq % 8, where the
+// Merge of the splits' partials: one wave per (unit, head), a lane per 16
+// contiguous bytes of a head's partial (8 columns, two n32 positions times the
+// four column blocks of the layout above); the wave of a head of sequence sq runs on XCD sq % 8, where the
 // decode workgroups of sq wrote the partials (so they are read from that L2).
 // kS is the split count rounded up to 2, 4, 8 or 16.  Every load is issued
 // before any is used (one round trip): each split's 16 bytes of the lane's
@@ -976,9 +981,11 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(
     }
     const int head = (unit % groups) * hg_size + h;
     const float inv = L > 0.f ? 1.0f / L : 0.f;
-    float4_t *orow = reinterpret_cast<float4_t *>(out + ((int64_t)b * heads + head) * kLatent + 8 * lane);
-    orow[0] = float4_t{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-    orow[1] = float4_t{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+    // acc[4 j + cb]: column 128 (lane / 16) + 32 cb + 2 (lane % 16) + j
+    float *orow = out + ((int64_t)b * heads + head) * kLatent + 128 * (lane >> 4) + 2 * (lane & 15);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+        *reinterpret_cast<float2_t *>(orow + 32 * cb) = float2_t{acc[cb] * inv, acc[4 + cb] * inv};
     if (lane == 0)
         lse[(int64_t)b * heads + head] =
             L > 0.f ? (M + log2f(L)) * 0.69314718055994530942f : -INFINITY;
