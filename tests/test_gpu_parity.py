@@ -142,6 +142,10 @@ DECODE_CASES = [
     (2, 64, [333, 129], 17, dict(junk=3)),
     (1, 64, [70000], 2048, {}),
     (6, 16, [64, 65, 127, 128, 129, 1], 64, {}),
+    # split counts that are not a power of two (11 and 7): the merge's
+    # padded split slots carry weight 0
+    (12, 64, [4100, 2049, 3000, 150, 5000, 2048, 64, 999, 4444, 2500, 1, 3333], 2048, {}),
+    (40, 16, [1200 + 97 * i for i in range(40)], 1024, dict(pad=300)),
 ]
 
 
