@@ -905,10 +905,14 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     // head's 512 values in the order the value waves hold them, so that a
     // lane writes its four column blocks as one 8-byte store (column
     // 128 sw + 32 cb + n32) -- and part_ml [unit][split][HG][2] = (running
-    // max in log2 units, sum).  The partials are streamed past the L2
-    // (non-temporal stores), which leaves the L2 to the rows still being
-    // gathered.
+    // max in log2 units, sum).  Where other workgroups on this XCD read the
+    // same rows again (two head groups, or several query tokens) the partials
+    // are streamed past the L2 (non-temporal stores), which leaves the L2 to
+    // those rows.  Otherwise (16 heads, one token) no row is read twice, and
+    // ordinary stores leave the partials in the L2 for the merge, which runs
+    // on the same XCD.
     const size_t pidx = (size_t)unit * splits + split;
+    const bool keep_in_l2 = MB == 1 && tokens == 1;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int h = 8 * (i >> 2) + 4 * g2 + (i & 3);
@@ -917,8 +921,11 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         const half4_t x4 = {(_Float16)(o[0][i] * inv), (_Float16)(o[1][i] * inv), (_Float16)(o[2][i] * inv),
                             (_Float16)(o[3][i] * inv)};
-        __builtin_nontemporal_store(__builtin_bit_cast(uint64_t, x4),
-                                    reinterpret_cast<uint64_t *>(part_o) + (pidx * HG + h) * 128 + sw * 32 + n32);
+        uint64_t *dst = reinterpret_cast<uint64_t *>(part_o) + (pidx * HG + h) * 128 + sw * 32 + n32;
+        if (keep_in_l2)
+            *dst = __builtin_bit_cast(uint64_t, x4);
+        else
+            __builtin_nontemporal_store(__builtin_bit_cast(uint64_t, x4), dst);
     }
     if (vt < HG) {
         const float l_tot = sum_lds[0][vt] + sum_lds[1][vt] + sum_lds[2][vt] + sum_lds[3][vt];
