@@ -934,10 +934,12 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     }
 }
 
-// Merge of the splits' partials: one wave per (unit, head), a lane per 16
-// contiguous bytes of a head's partial (8 columns, two n32 positions times the
-// four column blocks of the layout above); the wave of a head of sequence sq runs on XCD sq % 8, where the
-// decode workgroups of sq wrote the partials (so they are read from that L2).
+// Merge of the splits' partials: one single-wave workgroup per (unit, head)
+// (four-wave workgroups were slower by 0.1-0.3 us per call), a lane per 16
+// contiguous bytes of a head's partial (8 columns, two n32 positions times
+// the four column blocks of the layout above); the wave of a head of
+// sequence sq runs on XCD sq % 8, where the decode workgroups of sq wrote
+// the partials (so they are read from that L2).
 // kS is the split count rounded up to 2, 4, 8 or 16.  Every load is issued
 // before any is used (one round trip): each split's 16 bytes of the lane's
 // columns, and, in lane s, the (m, l) of split s, which every lane then
@@ -946,12 +948,12 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
 //   M = max_s m_s,  w_s = 2^(m_s - M) l_s,  out = sum_s w_s O_s / sum_s w_s,
 //   lse = ln 2 * (M + log2 sum_s w_s).
 template <int kS>
-__global__ __launch_bounds__(256) void merge_splits_kernel(
+__global__ __launch_bounds__(64) void merge_splits_kernel(
     const _Float16 *__restrict__ part_o, const float *__restrict__ part_ml,
     float *__restrict__ out, float *__restrict__ lse, int32_t heads, int32_t hg_size,
     int32_t groups, int32_t splits, int32_t batch, int32_t tokens) {
     const int xcd = blockIdx.x & 7;
-    const int p = __builtin_amdgcn_readfirstlane((int)(blockIdx.x >> 3) * 4 + (int)(threadIdx.x >> 6));
+    const int p = __builtin_amdgcn_readfirstlane((int)(blockIdx.x >> 3));
     const int per_seq = groups * hg_size;
     const int r_seq = p / per_seq;
     const int sq = (r_seq / tokens) * 8 + xcd;
@@ -1062,11 +1064,12 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
 #undef SMLA_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
-    // one wave per (unit, head); the blocks of XCD x take the sequences sq = x mod 8
+    // one single-wave workgroup per (unit, head); the blocks of XCD x take the
+    // sequences sq = x mod 8
     const int64_t per_xcd =
         (int64_t)((batch + 7) / 8) * tokens * plan.groups * plan.heads_per_group;
-    const dim3 mg((unsigned)(8 * ((per_xcd + 3) / 4)));
-#define SMLA_MERGE(S) hipLaunchKernelGGL((merge_splits_kernel<S>), mg, dim3(256), 0, stream, part_o, part_ml, \
+    const dim3 mg((unsigned)(8 * per_xcd));
+#define SMLA_MERGE(S) hipLaunchKernelGGL((merge_splits_kernel<S>), mg, dim3(64), 0, stream, part_o, part_ml, \
                                          out, lse, heads, plan.heads_per_group, plan.groups, plan.splits, \
                                          batch, tokens)
     if (plan.splits <= 2) SMLA_MERGE(2);
