@@ -24,7 +24,13 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# SMLA_ORACLE_SANITIZE=1 selects a second build of the same source with
+# AddressSanitizer and UndefinedBehaviorSanitizer (the process must preload
+# their runtimes; tests/test_oracle_sanitize.py does this).
+_SANITIZE = os.environ.get("SMLA_ORACLE_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+              "-fno-omit-frame-pointer", "-g"]
 
 ROW_BYTES = 352
 FP8_ROW_BYTES = 576
@@ -40,7 +46,8 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-               "-fPIC", "-shared", "-std=c11", "-Wall", "-o", tmp, _SRC, "-lm"]
+               "-fPIC", "-shared", "-std=c11", "-Wall", *(_SAN_FLAGS if _SANITIZE else []),
+               "-o", tmp, _SRC, "-lm"]
         subprocess.check_call(cmd)
         os.replace(tmp, _LIB)
     return _LIB

@@ -127,6 +127,26 @@ def _req(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _req_shape(t: torch.Tensor, name: str, dtype, shape: tuple, device):
+    _req(t, name, dtype, len(shape), device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _req_workspace(ws, device) -> tuple:
+    """(pointer, bytes) of a caller-supplied workspace: a contiguous tensor
+    on the call's device (any dtype), or (None, 0)."""
+    if ws is None:
+        return None, 0
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if not ws.is_cuda or ws.device != device:
+        raise ValueError("workspace is on %s, expected %s" % (ws.device, device))
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
 def version() -> int:
     return int(lib.smla_version())
 
@@ -194,16 +214,15 @@ def _decode(q, cache, page_table, seq_lens, topk, softmax_scale, out, lse, works
     if out is None:
         out = torch.empty((B, H, LATENT), dtype=torch.float32, device=dev)
     else:
-        _req(out, "out", torch.float32, 3, dev)
+        _req_shape(out, "out", torch.float32, (B, H, LATENT), dev)
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     else:
-        _req(lse, "lse", torch.float32, 2, dev)
+        _req_shape(lse, "lse", torch.float32, (B, H), dev)
     need = int(ws_fn(B, H, K))
     if workspace is None and need > 0:
         workspace = workspace_for(dev, need, stream)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _req_workspace(workspace, dev)
     _check(fn(q.data_ptr(), cache.data_ptr(), cache.shape[0], page_table.data_ptr(),
               page_table.shape[1], seq_lens.data_ptr(), topk.data_ptr(), B, H, K,
               float(softmax_scale), out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes,
@@ -335,10 +354,9 @@ def topk_select(scores: torch.Tensor, seq_lens: torch.Tensor, topk: int,
             raise ValueError("out must be [B, topk]")
     if workspace is None:
         workspace = topk_workspace(dev, B, ld, stream)
+    ws_ptr, ws_bytes = _req_workspace(workspace, dev)
     _check(lib.smla_topk_select(scores.data_ptr(), ld, seq_lens.data_ptr(), B, int(topk),
-                                out.data_ptr(), workspace.data_ptr(),
-                                workspace.numel() * workspace.element_size(),
-                                _stream_ptr(dev, stream)))
+                                out.data_ptr(), ws_ptr, ws_bytes, _stream_ptr(dev, stream)))
     return out
 
 
@@ -370,16 +388,15 @@ def sparse_mla_decode_mtp(q: torch.Tensor, cache: torch.Tensor, page_table: torc
     if out is None:
         out = torch.empty((B, T, H, LATENT), dtype=torch.float32, device=dev)
     else:
-        _req(out, "out", torch.float32, 4, dev)
+        _req_shape(out, "out", torch.float32, (B, T, H, LATENT), dev)
     if lse is None:
         lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     else:
-        _req(lse, "lse", torch.float32, 3, dev)
+        _req_shape(lse, "lse", torch.float32, (B, T, H), dev)
     need = decode_workspace_bytes_mtp(B, T, H, K)
     if workspace is None and need > 0:
         workspace = workspace_for(dev, need, stream)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _req_workspace(workspace, dev)
     _check(lib.smla_sparse_mla_decode_mtp(q.data_ptr(), cache.data_ptr(), cache.shape[0],
                                           page_table.data_ptr(), page_table.shape[1],
                                           seq_lens.data_ptr(), topk.data_ptr(), B, T, H, K,

@@ -32,6 +32,29 @@ def worst_head_rel(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.where(r > 0, d / np.maximum(r, 1e-300), d)))
 
 
+# The parity bars.  OUT_TOL and LSE_TOL are the stated ones: relative L2 of
+# out over the whole tensor, absolute error of lse.  HEAD_TOL is the same
+# relative L2 per (query, head) row of out, set from the arithmetic: the
+# GPU path's only rounding beyond fp32 summation order is the f16 softmax
+# weight (and the f16 split partial), 2^-11 relative each, so a head's error
+# stays near 1e-3 at worst; 5e-3 leaves headroom while a systematic error in
+# one head group, split or token (a dropped tile, a wrong scale) still fails.
+OUT_TOL = 2e-2
+LSE_TOL = 1e-3
+HEAD_TOL = 5e-3
+
+
+def check_parity(got_o, ref_o, got_l, ref_l, what: str = ""):
+    """Assert the three bars; returns (rel_l2, worst_head_rel, lse_err)."""
+    e_out, e_worst, e_lse = rel_l2(got_o, ref_o), worst_head_rel(got_o, ref_o), lse_err(got_l, ref_l)
+    note("  %s rel_l2 %.3e worst-head %.3e lse %.3e" % (what, e_out, e_worst, e_lse))
+    assert np.isfinite(np.asarray(got_o)).all(), what
+    assert e_out <= OUT_TOL, (what, e_out)
+    assert e_worst <= HEAD_TOL, (what, e_worst)
+    assert e_lse <= LSE_TOL, (what, e_lse)
+    return e_out, e_worst, e_lse
+
+
 def lse_err(got: np.ndarray, ref: np.ndarray) -> float:
     g = got.astype(np.float64)
     both_inf = np.isneginf(g) & np.isneginf(ref)

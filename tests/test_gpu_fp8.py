@@ -9,9 +9,9 @@ import torch
 
 import oracle
 import workloads as wl
-from cases import (gpu_cache, gpu_decode, lse_err, note, oracle_cache, oracle_decode, rel_l2,
-                   small_case, to_dev_bf16, worst_head_rel)
-from test_gpu_parity import (DECODE_CASES, LSE_TOL, OUT_TOL, _ascending_lists,
+from cases import (check_parity, gpu_cache, gpu_decode, note, oracle_cache, oracle_decode,
+                   small_case, to_dev_bf16)
+from test_gpu_parity import (DECODE_CASES, _ascending_lists,
                              _full_workload_check, _max_moves, _shared_pages_case)
 
 pytestmark = pytest.mark.gpu
@@ -100,10 +100,7 @@ def test_fp8_decode_matches_oracle(dev, smla, batch, heads, lens, topk, kw):
     assert np.array_equal(cache_d.cpu().numpy(), cache_o)
     out, lse = gpu_decode(case, cache_d, dev, smla)
     ref_o, ref_l = oracle_decode(case, cache_o)
-    e_out, e_worst, e_lse = rel_l2(out, ref_o), worst_head_rel(out, ref_o), lse_err(lse, ref_l)
-    note("  rel_l2 %.3e worst-head %.3e lse %.3e" % (e_out, e_worst, e_lse))
-    assert np.isfinite(out).all()
-    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+    check_parity(out, ref_o, lse, ref_l)
 
 
 def test_fp8_decode_empty_selections(dev, smla):
@@ -149,10 +146,7 @@ def test_fp8_decode_running_max_moves(dev, smla, batch, heads):
     assert np.array_equal(cache_d.cpu().numpy(), cache_o)
     out, lse = gpu_decode(case, cache_d, dev, smla)
     ref_o, ref_l = oracle_decode(case, cache_o)
-    e_out, e_lse = rel_l2(out, ref_o), lse_err(lse, ref_l)
-    note("  rel_l2 %.3e lse %.3e" % (e_out, e_lse))
-    assert np.isfinite(out).all()
-    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+    check_parity(out, ref_o, lse, ref_l)
 
 
 def test_fp8_full_tp4(dev, smla):

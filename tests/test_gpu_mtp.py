@@ -1,6 +1,7 @@
 """GPU parity of the multi-token (MTP) decode against the CPU oracle, through
 the C ABI.  Same bars as the single-token decode: out within 2e-2 relative L2
-over the whole [B,T,H,512] tensor, lse within 1e-3 absolute.
+over the whole [B,T,H,512] tensor and 5e-3 per (sequence, token, head), lse
+within 1e-3 absolute.
 """
 import numpy as np
 import pytest
@@ -8,8 +9,7 @@ import torch
 
 import oracle
 import workloads as wl
-from cases import gpu_cache, lse_err, note, oracle_cache, rel_l2, small_case, to_dev_bf16
-from test_gpu_parity import LSE_TOL, OUT_TOL
+from cases import check_parity, gpu_cache, note, oracle_cache, small_case, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -81,10 +81,7 @@ def test_mtp_matches_oracle(dev, smla, batch, tokens, heads, lens, topk):
     ref_o, ref_l = oracle.sparse_mla_decode_mtp(case["q"], cache_o, case["pt"], case["lens"],
                                                 case["topk"], case["scale"])
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
-    e_out, e_lse = rel_l2(out, ref_o), lse_err(lse, ref_l)
-    note("  rel_l2 %.3e lse %.3e" % (e_out, e_lse))
-    assert np.isfinite(out).all()
-    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+    check_parity(out, ref_o, lse, ref_l)
 
 
 def test_mtp_one_token_is_the_plain_decode(dev, smla):
@@ -102,8 +99,27 @@ def test_mtp_one_token_is_the_plain_decode(dev, smla):
     assert torch.equal(o1, o2[:, 0]) and torch.equal(l1, l2[:, 0])
 
 
+def _sequence_mini_cache(w, b, positions, L, dev):
+    """The oracle's own cache for the given logical positions of sequence b:
+    every logical page holding one of them gets a page of its own, with the
+    position's row quantised by the oracle from the regenerated BF16 row.
+    Returns (cache [P,64,352], page table [1, ceil(L/64)])."""
+    pos = np.unique(np.asarray(positions, dtype=np.int64))
+    pages = np.unique(pos // 64)
+    pt = np.full((1, (L + 63) // 64), -1, dtype=np.int32)
+    pt[0, pages] = np.arange(pages.size, dtype=np.int32)
+    cache = np.zeros((pages.size, 64, 352), dtype=np.uint8)
+    rows = oracle.quant_rows(wl.bf16_bits(wl.rows_at(w, 0, b, pos, device=dev)))
+    cache.reshape(-1, 352)[pt[0, pos // 64].astype(np.int64) * 64 + pos % 64] = rows
+    return cache, pt
+
+
 @pytest.mark.parametrize("name,tokens,sample", [("tp4", 4, [0, 31]), ("allheads", 2, [0, 63])])
 def test_mtp_full_workload_sampled(dev, smla, name, tokens, sample):
+    """Full-size caches and lists; a few entries of every token's list name the
+    newest positions, which only later tokens see, so each token's causal
+    limit decides.  The oracle gets the sequence length and computes each
+    token's limit itself; sampled sequences, every token and head checked."""
     w = wl.WORKLOADS[name]
     lens = wl.context_lengths(w, 0)
     pt_np, num_pages = wl.build_page_table(w, lens, 0)
@@ -111,6 +127,11 @@ def test_mtp_full_workload_sampled(dev, smla, name, tokens, sample):
     cache = torch.zeros((num_pages, 64, 352), dtype=torch.uint8, device=dev)
     wl.fill_cache(w, 0, lens, pt_np, lambda r, s: smla.kv_quant_append(r, s, cache), dev)
     tk = wl.mtp_topk(w, lens, tokens, 0)
+    newest = np.arange(tokens - 1, dtype=np.int64)          # L-T+1 .. L-1: seen by later tokens
+    for b in range(tk.shape[0]):
+        L = int(lens[b])
+        for j in range(tokens):
+            tk[b, j, 1:1 + newest.size] = (L - tokens + 1 + newest).astype(np.int32)
     q = torch.cat([wl.queries(w, 0, set_id=j, device=dev)[:, None] for j in range(tokens)], 1)
     out, lse = smla.sparse_mla_decode_mtp(q.contiguous(), cache, torch.as_tensor(pt_np, device=dev),
                                           torch.as_tensor(lens.astype(np.int32), device=dev),
@@ -119,20 +140,20 @@ def test_mtp_full_workload_sampled(dev, smla, name, tokens, sample):
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     assert np.isfinite(out).all() and np.isfinite(lse).all()
     qbits = wl.bf16_bits(q)
+    flat = cache.view(-1, 352)
     for b in sample:
-        for j in range(tokens):
-            sel = tk[b, j][tk[b, j] >= 0].astype(np.int64)
-            rows = oracle.quant_rows(wl.bf16_bits(wl.rows_at(w, 0, b, sel, device=dev)))
-            n = sel.size
-            mini = np.zeros(((n + 63) // 64, 64, 352), dtype=np.uint8)
-            mini.reshape(-1, 352)[:n] = rows
-            ro, rl = oracle.sparse_mla_decode(qbits[b, j][None], mini,
-                                              np.arange(mini.shape[0], dtype=np.int32)[None],
-                                              np.array([n]), np.arange(n, dtype=np.int32)[None],
+        L = int(lens[b])
+        sel = tk[b][tk[b] >= 0].astype(np.int64)
+        mini, mpt = _sequence_mini_cache(w, b, sel, L, dev)
+        # the device cache holds the same bytes at those positions
+        uniq = np.unique(sel)
+        slots = torch.as_tensor(pt_np[b, uniq // 64].astype(np.int64) * 64 + uniq % 64, device=dev)
+        assert np.array_equal(flat[slots].cpu().numpy(),
+                              mini.reshape(-1, 352)[mpt[0, uniq // 64].astype(np.int64) * 64
+                                                    + uniq % 64])
+        ro, rl = oracle.sparse_mla_decode_mtp(qbits[b:b + 1], mini, mpt, np.array([L]), tk[b:b + 1],
                                               w.softmax_scale)
-            e_out, e_lse = rel_l2(out[b, j][None], ro), lse_err(lse[b, j][None], rl)
-            note("  seq %d token %d: rel_l2 %.3e lse %.3e" % (b, j, e_out, e_lse))
-            assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+        check_parity(out[b:b + 1], ro, lse[b:b + 1], rl, "seq %d" % b)
     del cache
     torch.cuda.empty_cache()
 
@@ -177,10 +198,4 @@ def test_mtp_edge_cases(dev, smla):
     assert np.isfinite(out).all()
     assert np.isneginf(lse[1, 1]).all() and not out[1, 1].any()
     assert np.isneginf(lse[3, 0]).all() and not out[3, 0].any()
-    e_out, e_lse = rel_l2(out, ref_o), lse_err(lse, ref_l)
-    note("  rel_l2 %.3e lse %.3e" % (e_out, e_lse))
-    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
-    for b in range(4):
-        for j in range(T):
-            if np.isfinite(ref_l[b, j]).all():
-                assert rel_l2(out[b, j], ref_o[b, j]) <= OUT_TOL, (b, j)
+    check_parity(out, ref_o, lse, ref_l)

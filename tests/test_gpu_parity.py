@@ -1,7 +1,8 @@
 """GPU parity of the HIP path against the CPU oracle (through the C ABI).
 
 Bars: cache bytes bit-exact; decode out within 2e-2 relative L2 over the
-whole [B,H,512] tensor and lse within 1e-3 absolute (max over (b,h)).
+whole [B,H,512] tensor and within 5e-3 for every (b,h) row, lse within 1e-3
+absolute (max over (b,h)).
 """
 import numpy as np
 import pytest
@@ -9,13 +10,10 @@ import torch
 
 import oracle
 import workloads as wl
-from cases import (gpu_cache, gpu_decode, lse_err, note, oracle_cache, oracle_decode, rel_l2,
-                   small_case, to_dev_bf16, worst_head_rel)
+from cases import (HEAD_TOL, LSE_TOL, OUT_TOL, check_parity, gpu_cache, gpu_decode, lse_err, note,
+                   oracle_cache, oracle_decode, rel_l2, small_case, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
-
-OUT_TOL = 2e-2
-LSE_TOL = 1e-3
 
 
 @pytest.fixture(scope="module")
@@ -160,10 +158,7 @@ def test_decode_matches_oracle(dev, smla, batch, heads, lens, topk, kw):
     assert np.array_equal(cache_d.cpu().numpy(), cache_o)
     out, lse = gpu_decode(case, cache_d, dev, smla)
     ref_o, ref_l = oracle_decode(case, cache_o)
-    e_out, e_worst, e_lse = rel_l2(out, ref_o), worst_head_rel(out, ref_o), lse_err(lse, ref_l)
-    note("  rel_l2 %.3e worst-head %.3e lse %.3e" % (e_out, e_worst, e_lse))
-    assert np.isfinite(out).all()
-    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+    check_parity(out, ref_o, lse, ref_l)
 
 
 def test_decode_empty_selections(dev, smla):
@@ -182,6 +177,29 @@ def test_decode_empty_selections(dev, smla):
     out2, lse2 = gpu_decode(case2, gpu_cache(small_case(1, 16, [128], 64, seed=6), dev, smla),
                             dev, smla)
     assert not out2.any() and np.isneginf(lse2).all()
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_decode_page_table_narrower_than_context(dev, smla, fmt):
+    """seq_lens past max_pages * 64: entries whose page-table column does not
+    exist are skipped (no load), as the oracle skips them."""
+    note("decode with a page table narrower than the context (%s)" % fmt)
+    case = small_case(3, 64, [3000, 2500, 700], 1024, seed=71)
+    cache_o = oracle_cache(case, fmt)
+    cache_d = gpu_cache(case, dev, smla, fmt)
+    max_pages = 20                                      # tokens 0..1279 have a page
+    case["pt"] = np.ascontiguousarray(case["pt"][:, :max_pages])
+    assert ((case["topk"] >= 64 * max_pages).sum(axis=1)[:2] > 300).all()
+    out, lse = gpu_decode(case, cache_d, dev, smla)
+    ref_o, ref_l = oracle_decode(case, cache_o)
+    check_parity(out, ref_o, lse, ref_l)
+    # the same rows selected with the entries past the table removed: equal
+    # results (the usable entries keep their order)
+    case_k = dict(case, topk=np.where(case["topk"] < 64 * max_pages, case["topk"], -1)
+                  .astype(np.int32))
+    out_k, lse_k = gpu_decode(case_k, cache_d, dev, smla)
+    assert np.allclose(out_k, out, rtol=0, atol=1e-6) and np.array_equal(np.isneginf(lse_k),
+                                                                         np.isneginf(lse))
 
 
 def test_decode_deterministic(dev, smla):
@@ -300,10 +318,7 @@ def test_decode_running_max_moves(dev, smla, batch, heads):
     cache_d = gpu_cache(case, dev, smla)
     out, lse = gpu_decode(case, cache_d, dev, smla)
     ref_o, ref_l = oracle_decode(case, cache_o)
-    e_out, e_lse = rel_l2(out, ref_o), lse_err(lse, ref_l)
-    note("  rel_l2 %.3e lse %.3e" % (e_out, e_lse))
-    assert np.isfinite(out).all()
-    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+    check_parity(out, ref_o, lse, ref_l)
 
 
 # --------------------------------------------------------------------------
@@ -357,9 +372,7 @@ def _full_workload_check(dev, smla, name, sample, seed=0, fmt="nvfp4"):
                                           np.arange((n + 63) // 64, dtype=np.int32)[None],
                                           np.array([n]), np.arange(n, dtype=np.int32)[None],
                                           w.softmax_scale)
-        e_out, e_lse = rel_l2(out[b:b + 1], ro), lse_err(lse[b:b + 1], rl)
-        note("  seq %d: rel_l2 %.3e lse %.3e" % (b, e_out, e_lse))
-        assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+        e_out = check_parity(out[b:b + 1], ro, lse[b:b + 1], rl, "seq %d" % b)[0]
         worst = max(worst, e_out)
     del cache
     torch.cuda.empty_cache()
@@ -408,9 +421,7 @@ def test_decode_ignores_unselected_nan_row(dev, smla, fmt):
     ref_o, ref_l = oracle_decode(case, cache_o)
     assert np.isfinite(ref_o).all()
     assert np.isfinite(out).all() and np.isfinite(lse).all()
-    e_out, e_lse = rel_l2(out, ref_o), lse_err(lse, ref_l)
-    note("  rel_l2 %.3e lse %.3e" % (e_out, e_lse))
-    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+    check_parity(out, ref_o, lse, ref_l)
 
 
 def test_decode_max_batch(dev, smla):
@@ -443,9 +454,7 @@ def test_decode_max_batch(dev, smla):
         assert np.array_equal(got_bytes, mini[0]), "cache bytes differ for sequence %d" % b
         ro, rl = oracle.sparse_mla_decode(wl.bf16_bits(q[b:b + 1]), mini, np.zeros((1, 1), np.int32),
                                           np.array([L]), tk[b:b + 1].cpu().numpy(), 1.0 / np.sqrt(576.0))
-        e_out, e_lse = rel_l2(out[b:b + 1].cpu().numpy(), ro), lse_err(lse[b:b + 1].cpu().numpy(), rl)
-        note("  seq %d: rel_l2 %.3e lse %.3e" % (b, e_out, e_lse))
-        assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+        check_parity(out[b:b + 1].cpu().numpy(), ro, lse[b:b + 1].cpu().numpy(), rl, "seq %d" % b)
     del rows, q, out, lse, cache
     torch.cuda.empty_cache()
 
@@ -475,3 +484,40 @@ def test_decode_workspace_reuse_across_shapes(dev, smla):
         o2, l2 = fn(*args, workspace=fresh)
         torch.cuda.synchronize(dev)
         assert torch.equal(o1, o2) and torch.equal(l1, l2), trial
+
+
+def test_binding_rejects_misshaped_outputs_and_foreign_workspace(dev, smla):
+    """A caller-supplied out, lse or workspace that does not fit the call is
+    refused with ValueError before anything is launched (the buffers keep
+    their contents)."""
+    note("binding checks of out, lse and workspace")
+    case = small_case(2, 64, [3000, 1000], 512, seed=77)
+    cache_d = gpu_cache(case, dev, smla)
+    q = to_dev_bf16(case["q"], dev)
+    pt = torch.as_tensor(case["pt"], device=dev)
+    sl = torch.as_tensor(case["lens"].astype(np.int32), device=dev)
+    tk = torch.as_tensor(case["topk"], device=dev)
+    bad_out = torch.full((2, 16, 512), 7.0, device=dev)          # 16 heads for a 64-head q
+    bad_lse = torch.full((2, 63), 7.0, device=dev)
+    good_out = torch.full((2, 64, 512), 7.0, device=dev)
+    good_lse = torch.full((2, 64), 7.0, device=dev)
+    calls = [dict(out=bad_out), dict(lse=bad_lse), dict(out=good_out, lse=bad_lse),
+             dict(workspace=torch.zeros(1 << 20, dtype=torch.uint8)),               # host memory
+             dict(workspace=torch.zeros((1 << 20, 2), dtype=torch.uint8, device=dev)[:, 0])]
+    for kw in calls:
+        with pytest.raises(ValueError):
+            smla.sparse_mla_decode(q, cache_d, pt, sl, tk, case["scale"], **kw)
+    qm, tkm = q[:, None].contiguous(), tk[:, None].contiguous()
+    for kw in (dict(out=good_out), dict(lse=good_lse),
+               dict(workspace=torch.zeros(1 << 20, dtype=torch.uint8))):
+        with pytest.raises(ValueError):
+            smla.sparse_mla_decode_mtp(qm, cache_d, pt, sl, tkm, case["scale"], **kw)
+    torch.cuda.synchronize(dev)
+    for t in (bad_out, bad_lse, good_out, good_lse):
+        assert bool((t == 7.0).all())
+    # the same buffers, shaped right, are accepted
+    out, lse = smla.sparse_mla_decode(q, cache_d, pt, sl, tk, case["scale"], out=good_out,
+                                      lse=good_lse)
+    torch.cuda.synchronize(dev)
+    ref_o, ref_l = oracle_decode(case, oracle_cache(case))
+    check_parity(out.cpu().numpy(), ref_o, lse.cpu().numpy(), ref_l)

@@ -10,8 +10,7 @@ import torch
 
 import oracle
 import workloads as wl
-from cases import (gpu_cache, lse_err, note, oracle_cache, rel_l2, small_case, to_dev_bf16)
-from test_gpu_parity import LSE_TOL, OUT_TOL
+from cases import check_parity, gpu_cache, note, oracle_cache, small_case, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -106,9 +105,7 @@ def test_staged_copy_and_decode_match_oracle(dev, smla, batch, heads, lens, topk
     torch.cuda.synchronize(dev)
     spt, ssl = oracle.staged_tables(batch, topk)
     ref_o, ref_l = oracle.sparse_mla_decode(case["q"], want, spt, ssl, want_st, case["scale"])
-    e_out, e_lse = rel_l2(out.cpu().numpy(), ref_o), lse_err(lse.cpu().numpy(), ref_l)
-    note("  rel_l2 %.3e lse %.3e" % (e_out, e_lse))
-    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+    check_parity(out.cpu().numpy(), ref_o, lse.cpu().numpy(), ref_l)
 
 
 def test_staged_full_allheads_sampled(dev, smla):
@@ -144,8 +141,6 @@ def test_staged_full_allheads_sampled(dev, smla):
         assert np.array_equal(got[:n], want.reshape(-1, 576)[:n]), "staged rows differ, seq %d" % b
         spt, ssl = oracle.staged_tables(1, K)
         ro, rl = oracle.sparse_mla_decode(qbits[b:b + 1], want, spt, ssl, want_st, w.softmax_scale)
-        e_out, e_lse = rel_l2(out[b:b + 1], ro), lse_err(lse[b:b + 1], rl)
-        note("  seq %d: rel_l2 %.3e lse %.3e" % (b, e_out, e_lse))
-        assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+        check_parity(out[b:b + 1], ro, lse[b:b + 1], rl, "seq %d" % b)
     del cache, staged
     torch.cuda.empty_cache()

@@ -12,8 +12,7 @@ import torch
 
 import oracle
 import workloads as wl
-from cases import lse_err, note, rel_l2, to_dev_bf16
-from test_gpu_parity import LSE_TOL, OUT_TOL
+from cases import check_parity, note, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -156,6 +155,4 @@ def test_select_then_decode(dev, smla):
     ref_tk = oracle.topk_select(x, lens, 2048)
     ref_o, ref_l = oracle.sparse_mla_decode(case["q"], oracle_cache(case), case["pt"], lens,
                                             ref_tk, case["scale"])
-    e_out, e_lse = rel_l2(out.cpu().numpy(), ref_o), lse_err(lse.cpu().numpy(), ref_l)
-    note("  rel_l2 %.3e lse %.3e" % (e_out, e_lse))
-    assert e_out <= OUT_TOL and e_lse <= LSE_TOL
+    check_parity(out.cpu().numpy(), ref_o, lse.cpu().numpy(), ref_l)

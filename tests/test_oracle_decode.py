@@ -234,3 +234,27 @@ def test_oracle_on_generated_tiny_workload():
     ref_o, ref_l = library_attention(q[0], Kd, w.softmax_scale)
     np.testing.assert_allclose(out[0], ref_o, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(lse[0], ref_l, rtol=1e-13, atol=1e-13)
+
+
+def test_entries_past_the_page_table_are_skipped():
+    """A context longer than its page-table row (seq_lens > max_pages * 64):
+    an entry t with t / 64 >= max_pages has no page and is skipped, so the
+    result is attention over the selected rows the table does hold, computed
+    by the library routine over rows decoded without the oracle."""
+    case = make_case(B=2, H=3, lens=(300, 260), seed=17)
+    rng = np.random.default_rng(18)
+    topk = np.stack([rng.choice(300, 120, replace=False),
+                     rng.choice(260, 120, replace=False)]).astype(np.int32)
+    max_pages = 3                                    # tokens 0..191 have a page
+    narrow = np.ascontiguousarray(case["pt"][:, :max_pages])
+    assert (topk >= 64 * max_pages).sum(axis=1).min() > 20
+    out, lse = run(case, topk, pt=narrow)
+    for b in range(2):
+        sel = topk[b][topk[b] < 64 * max_pages]
+        ref_o, ref_l = library_attention(case["q"][b], decoded_logical(case, b)[sel], SCALE)
+        np.testing.assert_allclose(out[b], ref_o, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[b], ref_l, rtol=1e-13, atol=1e-13)
+    # only such entries: nothing usable
+    only_past = np.where(topk >= 64 * max_pages, topk, -1).astype(np.int32)
+    out2, lse2 = run(case, only_past, pt=narrow)
+    assert not out2.any() and np.isneginf(lse2).all()

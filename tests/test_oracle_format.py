@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+import workloads as wl
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
 E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])   # e2m1 magnitudes, by definition
@@ -282,3 +283,29 @@ def test_layout_constants_match_pages():
     assert round(sb["tokens"] * sb["layers"] * total / 1e9, 1) == sb["nvfp4_GB_1dp"]
     rq = g["request_bytes"]
     assert round(rq["tokens"] * rq["layers"] * total / 1e9, 1) == rq["nvfp4_GB_1dp"]
+
+
+def test_append_slot_rules():
+    """The paged append writes row i to slot s = page * 64 + row and skips a
+    slot outside [0, num_pages * 64): -1, -2^31, num_pages * 64 and 2^31 - 1.
+    The cache is a window of a larger array, so a row written just outside it
+    lands in a guard band that must stay untouched."""
+    P = 2
+    backing = np.full((P + 4, 64, 352), 0xAB, dtype=np.uint8)
+    cache = backing[2:2 + P]
+    assert cache.flags.c_contiguous
+    g = torch.Generator().manual_seed(31)
+    x = wl.bf16_bits(torch.randn((5, 576), generator=g).to(torch.bfloat16))
+    slots = np.array([5, -1, P * 64, 127, 64], dtype=np.int32)
+    assert oracle.kv_quant_append(x, slots, cache) == 3
+    rows = oracle.quant_rows(x)
+    flat = backing.reshape(-1, 352)
+    base = 2 * 64
+    want = np.full_like(flat, 0xAB)
+    want[base + 5], want[base + 127], want[base + 64] = rows[0], rows[3], rows[4]
+    assert np.array_equal(flat, want)
+    # the extreme int32 slots are skipped too (nothing written, nothing read)
+    far = np.array([-2 ** 31, 2 ** 31 - 1, 0], dtype=np.int32)
+    assert oracle.kv_quant_append(x[:3], far, cache) == 1
+    want[base + 0] = rows[2]
+    assert np.array_equal(flat, want)

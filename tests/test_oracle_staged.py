@@ -133,3 +133,27 @@ def test_lossy_copy_stays_close_to_the_fused_result():
     rel = np.linalg.norm(o2 - o1) / np.linalg.norm(o1)
     assert 0 < rel < 2 ** -4
     assert np.max(np.abs(l2 - l1)) < 0.5
+
+
+def test_staged_skips_entries_past_the_page_table():
+    """seq_lens past max_pages * 64: an entry whose page-table column does not
+    exist is unusable (staged_topk -1, its staged row untouched), like -1."""
+    case = make_case(B=2, H=2, lens=(250, 200), seed=25)
+    max_pages = 2                                        # tokens 0..127 have a page
+    narrow = np.ascontiguousarray(case["pt"][:, :max_pages])
+    topk = np.array([[5, 130, 127, 200, 249, 64],
+                     [128, 0, 199, 63, 150, 100]], dtype=np.int32)
+    init = np.full((2, 64, 576), 0x5A, dtype=np.uint8)
+    staged, st = oracle.stage_rows_fp8(case["cache"], narrow, case["lens"], topk, staged=init)
+    want = np.where(topk < 64 * max_pages, np.arange(6)[None, :], -1)
+    assert np.array_equal(st, want)
+    flat = staged.reshape(-1, 576)
+    for b in range(2):
+        for e in range(6):
+            t = int(topk[b, e])
+            if want[b, e] < 0:
+                assert (flat[b * 64 + e] == 0x5A).all()
+            else:
+                slot = int(narrow[b][t // 64]) * 64 + t % 64
+                src = case["cache"].reshape(-1, 352)[slot][None]
+                assert np.array_equal(flat[b * 64 + e], _library_stage(src)[0]), (b, e)
