@@ -81,11 +81,11 @@ size_t workspace_bytes(int32_t batch, int32_t tokens, int32_t heads, int32_t top
     return smla::plan_decode(batch, tokens, heads, topk, fmt).workspace_bytes;
 }
 
-int decode(const void *q_bf16, const uint8_t *cache, int64_t num_pages, const int32_t *page_table,
-           int32_t max_pages, const int32_t *seq_lens, const int32_t *topk_indices, int32_t batch,
-           int32_t tokens, int32_t heads, int32_t topk, float softmax_scale, float *out,
-           float *lse, void *workspace, size_t workspace_bytes, void *stream,
-           smla::RowFormat fmt) {
+// The checks of every decode argument except the workspace (host only).
+int check_decode_args(const void *q_bf16, const uint8_t *cache, int64_t num_pages,
+                      const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens,
+                      const int32_t *topk_indices, int32_t batch, int32_t tokens, int32_t heads,
+                      int32_t topk, const float *out, const float *lse) {
     if (heads != 16 && heads != 64) return SMLA_ERR_UNSUPPORTED;
     if (!batch_ok(batch, tokens) || topk < 1 || topk > SMLA_MAX_TOPK || max_pages < 1 ||
         num_pages < 1 || num_pages > ((int64_t)1 << 25))
@@ -95,6 +95,17 @@ int decode(const void *q_bf16, const uint8_t *cache, int64_t num_pages, const in
     if (!aligned(q_bf16, 16) || !aligned(out, 16) || !aligned(cache, 256) || !aligned(lse, 4) ||
         !aligned(page_table, 4) || !aligned(seq_lens, 4) || !aligned(topk_indices, 4))
         return SMLA_ERR_ALIGN;
+    return SMLA_OK;
+}
+
+int decode(const void *q_bf16, const uint8_t *cache, int64_t num_pages, const int32_t *page_table,
+           int32_t max_pages, const int32_t *seq_lens, const int32_t *topk_indices, int32_t batch,
+           int32_t tokens, int32_t heads, int32_t topk, float softmax_scale, float *out,
+           float *lse, void *workspace, size_t workspace_bytes, void *stream,
+           smla::RowFormat fmt) {
+    const int bad = check_decode_args(q_bf16, cache, num_pages, page_table, max_pages, seq_lens,
+                                      topk_indices, batch, tokens, heads, topk, out, lse);
+    if (bad != SMLA_OK) return bad;
     const smla::DecodePlan plan = smla::plan_decode(batch, tokens, heads, topk, fmt);
     if (plan.workspace_bytes > 0) {
         if (!workspace || workspace_bytes < plan.workspace_bytes) return SMLA_ERR_WORKSPACE;
@@ -216,3 +227,4 @@ int smla_sparse_mla_decode_mtp(const void *q_bf16, const uint8_t *cache, int64_t
 }
 
 }  // extern "C"
+

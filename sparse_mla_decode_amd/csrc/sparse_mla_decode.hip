@@ -46,21 +46,14 @@
 //     merge inside the first launch would need an agent-scope release per
 //     workgroup, an L2 writeback, which costs more than the launch).
 #include "smla_internal.h"
+#include "decode_device.h"
 
 #include <type_traits>
 
 namespace smla {
 namespace {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef float float16_t __attribute__((ext_vector_type(16)));
-typedef int int2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) int2_t lds_int2_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
+using namespace dev;
 
 constexpr int kThreads = 512;                   // 4 score waves + 4 value waves, two per SIMD
 constexpr int kTile = 64;                       // selected rows per tile (16 per wave)
@@ -96,91 +89,6 @@ template <> struct Ring<kFmtFp8> {
 // transposing reads of 8 rows x 4 column windows then spread over all LDS
 // banks instead of the two that a 576-byte row stride leaves them.
 __device__ __forceinline__ int fp8_swz(int r) { return ((r >> 1) & 3) << 1; }
-
-// NVFP4 tiles are stored with the 16-byte pieces of row r swapped in pairs
-// when bit 3 of r is set (piece p at p ^ nv_swz(r)): 16 consecutive rows then
-// start in 16 different 16-byte bank groups (a 352-byte row stride alone
-// repeats them every 8 rows), for the score waves' 16-byte row reads and
-// the value waves' transposing reads alike.
-__device__ __forceinline__ int nv_swz(int r) { return (r >> 3) & 1; }
-
-__device__ __forceinline__ half8_t join(half2_t a, half2_t b, half2_t c, half2_t d) {
-    half8_t r;
-    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-    return r;
-}
-
-// Reductions over the 16 lanes of a row with DPP lane moves (quad swaps,
-// half-row mirror, row mirror); every lane ends with the same value.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                 CTRL, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float row16_max(float x) {
-    x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
-    x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
-    x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
-    x = fmaxf(x, dpp<0x140>(x));  // row_mirror
-    return x;
-}
-__device__ __forceinline__ float row16_sum(float x) {
-    x += dpp<0xB1>(x);
-    x += dpp<0x4E>(x);
-    x += dpp<0x141>(x);
-    x += dpp<0x140>(x);
-    return x;
-}
-
-// two BF16 values (low half first) -> two f16, rounded to nearest even
-__device__ __forceinline__ half2_t bf16x2_to_f16x2(uint32_t w) {
-    const float2_t f = {__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)};
-    return __builtin_convertvector(f, half2_t);
-}
-
-// e2m1 pair (byte SEL of w) -> f16 pair, exact
-template <int SEL>
-__device__ __forceinline__ half2_t fp4x2(uint32_t w) {
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
-}
-// E4M3 pair (bytes 0,1 if HI is false, else 2,3 of w) -> f16 pair, exact
-template <bool HI>
-__device__ __forceinline__ half2_t fp8x2(uint32_t w) {
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
-}
-
-// One wave-wide direct-to-LDS load: lane l's 16 bytes at gptr go to LDS
-// byte lds_addr + 16 l.  Written as inline assembly so that the compiler does
-// not insert its own (full) waits for it before later LDS reads; the tile
-// ring waits for these loads explicitly with wait_vmcnt.
-__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(gptr), "s"(lds_addr)
-                 : "memory", "m0");
-}
-
-// Wait until at most N of this wave's memory loads are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_n() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Wait until at most n of this wave's memory loads are outstanding (n is
-// wave-uniform and one of the counts the tile ring produces).
-__device__ __forceinline__ void wait_vmcnt(int n) {
-    switch (n) {
-#define SMLA_WAIT(N) case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
-        SMLA_WAIT(0) SMLA_WAIT(1) SMLA_WAIT(2) SMLA_WAIT(3) SMLA_WAIT(4) SMLA_WAIT(5)
-        SMLA_WAIT(6) SMLA_WAIT(7) SMLA_WAIT(8) SMLA_WAIT(9) SMLA_WAIT(10) SMLA_WAIT(11)
-        SMLA_WAIT(12) SMLA_WAIT(13) SMLA_WAIT(14) SMLA_WAIT(15) SMLA_WAIT(16) SMLA_WAIT(17)
-        SMLA_WAIT(18) SMLA_WAIT(19) SMLA_WAIT(20) SMLA_WAIT(21) SMLA_WAIT(22) SMLA_WAIT(23)
-        SMLA_WAIT(24)
-#undef SMLA_WAIT
-        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    }
-}
 
 template <int MB, int FMT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -1002,9 +910,15 @@ __global__ __launch_bounds__(64) void merge_splits_kernel(
 
 }  // namespace
 
+constexpr bool kUseH64 = false;
+
 DecodePlan plan_decode(int batch, int tokens, int heads, int topk, RowFormat fmt) {
     DecodePlan p;
-    p.heads_per_group = heads >= 32 ? 32 : 16;
+    // NVFP4 rows at 64 heads may take the kernel of decode_h64.hip, one
+    // workgroup per (query, split) serving all 64 heads; it stays unselected
+    // while it is slower than two head groups of 32 at 64 heads
+    p.h64 = kUseH64 && fmt == kFmtNvfp4 && heads == 64;
+    p.heads_per_group = p.h64 ? 64 : heads >= 32 ? 32 : 16;
     p.groups = heads / p.heads_per_group;
     const int units = batch * tokens * p.groups;
     const int target = 256;  // one workgroup per CU
@@ -1014,7 +928,8 @@ DecodePlan plan_decode(int batch, int tokens, int heads, int topk, RowFormat fmt
     s = s > max_s ? max_s : s;
     s = s > kMaxSplits ? kMaxSplits : s;
     // a split scans at most the row ids its LDS holds
-    const int max_per = fmt == kFmtFp8 ? Ring<kFmtFp8>::kMaxPerSplit : Ring<kFmtNvfp4>::kMaxPerSplit;
+    const int max_per = p.h64 ? h64_max_per_split()
+                        : fmt == kFmtFp8 ? Ring<kFmtFp8>::kMaxPerSplit : Ring<kFmtNvfp4>::kMaxPerSplit;
     const int min_s = (topk + max_per - 1) / max_per;
     s = s < min_s ? min_s : s;
     p.splits = s;
@@ -1030,6 +945,29 @@ DecodePlan plan_decode(int batch, int tokens, int heads, int topk, RowFormat fmt
     }
     return p;
 }
+
+namespace {
+
+// one single-wave workgroup per (unit, head); the blocks of XCD x take the
+// sequences sq = x mod 8
+hipError_t launch_merge(const _Float16 *part_o, const float *part_ml, float *out, float *lse,
+                        int heads, const DecodePlan &plan, int batch, int tokens,
+                        hipStream_t stream) {
+    const int64_t per_xcd =
+        (int64_t)((batch + 7) / 8) * tokens * plan.groups * plan.heads_per_group;
+    const dim3 mg((unsigned)(8 * per_xcd));
+#define SMLA_MERGE(S) hipLaunchKernelGGL((merge_splits_kernel<S>), mg, dim3(64), 0, stream, part_o, part_ml, \
+                                         out, lse, heads, plan.heads_per_group, plan.groups, plan.splits, \
+                                         batch, tokens)
+    if (plan.splits <= 2) SMLA_MERGE(2);
+    else if (plan.splits <= 4) SMLA_MERGE(4);
+    else if (plan.splits <= 8) SMLA_MERGE(8);
+    else SMLA_MERGE(16);
+#undef SMLA_MERGE
+    return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int64_t num_pages,
                                     const int32_t *page_table, int32_t max_pages,
@@ -1049,6 +987,13 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
                                             ((o_bytes + 255) & ~(size_t)255));
     }
     const float scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    if (plan.h64) {
+        const hipError_t e = launch_decode_h64(q, cache, num_pages, page_table, max_pages, seq_lens,
+                                               topk_idx, batch, tokens, topk, scale_log2, out, lse,
+                                               part_o, part_ml, plan.splits, plan.per_split, stream);
+        if (e != hipSuccess || plan.splits == 1) return e;
+        return launch_merge(part_o, part_ml, out, lse, heads, plan, batch, tokens, stream);
+    }
 #define SMLA_LAUNCH(MB, FMT)                                                                 \
     hipLaunchKernelGGL((sparse_mla_decode_kernel<MB, FMT>), dim3(blocks), dim3(kThreads), 0, stream, \
                        q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,      \
@@ -1064,20 +1009,7 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
 #undef SMLA_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
-    // one single-wave workgroup per (unit, head); the blocks of XCD x take the
-    // sequences sq = x mod 8
-    const int64_t per_xcd =
-        (int64_t)((batch + 7) / 8) * tokens * plan.groups * plan.heads_per_group;
-    const dim3 mg((unsigned)(8 * per_xcd));
-#define SMLA_MERGE(S) hipLaunchKernelGGL((merge_splits_kernel<S>), mg, dim3(64), 0, stream, part_o, part_ml, \
-                                         out, lse, heads, plan.heads_per_group, plan.groups, plan.splits, \
-                                         batch, tokens)
-    if (plan.splits <= 2) SMLA_MERGE(2);
-    else if (plan.splits <= 4) SMLA_MERGE(4);
-    else if (plan.splits <= 8) SMLA_MERGE(8);
-    else SMLA_MERGE(16);
-#undef SMLA_MERGE
-    return hipGetLastError();
+    return launch_merge(part_o, part_ml, out, lse, heads, plan, batch, tokens, stream);
 }
 
 }  // namespace smla

@@ -11,7 +11,7 @@ import oracle
 import workloads as wl
 from cases import (check_parity, gpu_cache, gpu_decode, note, oracle_cache, oracle_decode,
                    small_case, to_dev_bf16)
-from test_gpu_parity import (DECODE_CASES, _ascending_lists,
+from test_gpu_parity import (DECODE_CASES, _ascending_lists, _plan,
                              _full_workload_check, _max_moves, _shared_pages_case)
 
 pytestmark = pytest.mark.gpu
@@ -139,8 +139,7 @@ def test_fp8_decode_running_max_moves(dev, smla, batch, heads):
     case, scores = _ascending_lists(case, cache_o, 16.0)
     # an FP8 workgroup covers at most 1024 list entries, so the list is cut
     # into at least two splits
-    units = batch * max(1, heads // 32)
-    splits = max(2, min(-(-256 // units), 2048 // 64, 16))
+    units, splits = _plan(batch, heads, 2048, fp8=True)
     assert _max_moves(scores, splits) >= units * splits
     cache_d = gpu_cache(case, dev, smla, "fp8")
     assert np.array_equal(cache_d.cpu().numpy(), cache_o)

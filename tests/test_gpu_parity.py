@@ -288,6 +288,23 @@ def _max_moves(scores, splits, slack=8.0):
     return moves
 
 
+# whether the library serves 64-head NVFP4 queries with its 64-head kernel
+H64_KERNEL = False
+
+
+def _plan(batch, heads, topk, fp8=False):
+    """Workgroups sharing a list and the split count of the library's plan:
+    with the 64-head kernel, 64-head NVFP4 queries take one workgroup per
+    (query, split) of at most 1024 entries; otherwise head groups of 32 (16)
+    and splits of at most 2048 (FP8: 1024) entries; about 256 workgroups, at
+    most 16 splits."""
+    h64 = H64_KERNEL and heads == 64 and not fp8
+    units = batch * (1 if h64 else max(1, heads // 32))
+    splits = max(1, min(-(-256 // units), -(-topk // 64), 16))
+    cap = 1024 if (h64 or fp8) else 2048
+    return units, max(splits, -(-topk // cap))
+
+
 def _shared_pages_case(batch, heads, pages, topk, seed):
     """batch sequences whose page tables are permutations of the same
     `pages` physical pages (one shared context), each with its own query and
@@ -311,11 +328,25 @@ def test_decode_running_max_moves(dev, smla, batch, heads):
     case = _shared_pages_case(batch, heads, 40, 2048, seed=40 + heads)
     cache_o = oracle_cache(case)
     case, scores = _ascending_lists(case, cache_o, 16.0)
-    units = batch * max(1, heads // 32)
-    splits = min(-(-256 // units), 2048 // 64, 16)
+    units, splits = _plan(batch, heads, 2048)
     # the re-weight path runs, on average, at least once per workgroup
     assert _max_moves(scores, splits) >= units * splits
     cache_d = gpu_cache(case, dev, smla)
+    out, lse = gpu_decode(case, cache_d, dev, smla)
+    ref_o, ref_l = oracle_decode(case, cache_o)
+    check_parity(out, ref_o, lse, ref_l)
+
+
+def test_decode_64_heads_long_splits(dev, smla):
+    """128 queries of 64 heads: one split per workgroup (two of 1024 entries
+    with the 64-head kernel, one of 2048 with head groups), sixteen or more
+    tiles per workgroup, so the tile pipeline runs long; every query and head
+    against the oracle."""
+    note("decode B=128 H=64 K=2048 (long splits)")
+    case = _shared_pages_case(128, 64, 40, 2048, seed=88)
+    assert _plan(128, 64, 2048) == ((128, 2) if H64_KERNEL else (256, 1))
+    cache_d = gpu_cache(case, dev, smla)
+    cache_o = oracle_cache(case)
     out, lse = gpu_decode(case, cache_d, dev, smla)
     ref_o, ref_l = oracle_decode(case, cache_o)
     check_parity(out, ref_o, lse, ref_l)
