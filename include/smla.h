@@ -79,7 +79,8 @@ enum {
     SMLA_ERR_ALIGN = -4,       /* a pointer is not aligned as documented       */
     SMLA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required   */
     SMLA_ERR_LAUNCH = -6,      /* the HIP runtime rejected a kernel launch     */
-    SMLA_ERR_DEVICE = -7       /* no usable gfx950 device is current           */
+    SMLA_ERR_DEVICE = -7,      /* no usable gfx950 device is current           */
+    SMLA_ERR_SCRATCH = -8      /* the shape needs more than the static scratch */
 };
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -281,6 +282,36 @@ size_t smla_topk_workspace_bytes(int32_t batch, int64_t ld);
 int smla_topk_select(const float *scores, int64_t ld, const int32_t *seq_lens, int32_t batch,
                      int32_t topk, int32_t *topk_indices, void *workspace, size_t workspace_bytes,
                      void *stream);
+
+/*
+ * ---- Decode that allocates nothing, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc) ----
+ *
+ * smla_sparse_mla_decode with the same arguments, meaning, conventions and
+ * errors, minus the workspace: the split partials go to a scratch array the
+ * library holds in device memory (a static device array of
+ * SMLA_NOALLOC_SCRATCH_BYTES on every GPU the library runs on, kept until the
+ * process ends).  The call performs no allocation of any kind.  A shape
+ * whose split partials need more than SMLA_NOALLOC_SCRATCH_BYTES (that is,
+ * smla_decode_workspace_bytes(batch, heads, topk) > SMLA_NOALLOC_SCRATCH_BYTES)
+ * is refused with SMLA_ERR_SCRATCH before anything is launched; every other
+ * shape smla_sparse_mla_decode takes is accepted, with bit-identical results.
+ *
+ * All calls on one GPU share that GPU's scratch array: two calls that
+ * overlap in time on the same GPU (different streams, or different host
+ * threads without ordering) race on it and give undefined results.  Calls
+ * ordered on one stream are safe.  The first call on a device looks up the
+ * array's device address (once per device, cached); that lookup can return
+ * SMLA_ERR_DEVICE.
+ */
+#define SMLA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+int smla_sparse_mla_decode_noalloc(const void *q_bf16, const uint8_t *cache, int64_t num_pages,
+                                   const int32_t *page_table, int32_t max_pages,
+                                   const int32_t *seq_lens, const int32_t *topk_indices,
+                                   int32_t batch, int32_t heads, int32_t topk,
+                                   float softmax_scale, float *out, float *lse, void *stream);
 
 #ifdef __cplusplus
 }

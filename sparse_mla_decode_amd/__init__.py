@@ -41,14 +41,16 @@ MAX_TOPK = 2048
 ERRORS = {
     0: "SMLA_OK", -1: "SMLA_ERR_NULL", -2: "SMLA_ERR_SHAPE", -3: "SMLA_ERR_UNSUPPORTED",
     -4: "SMLA_ERR_ALIGN", -5: "SMLA_ERR_WORKSPACE", -6: "SMLA_ERR_LAUNCH", -7: "SMLA_ERR_DEVICE",
+    -8: "SMLA_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 32 << 20   # SMLA_NOALLOC_SCRATCH_BYTES
 
 # exported symbols, in the order include/smla.h declares them
 EXPORTS = ("smla_strerror", "smla_version", "smla_kv_quant_append",
            "smla_decode_workspace_bytes", "smla_sparse_mla_decode", "smla_kv_quant_append_fp8",
            "smla_decode_workspace_bytes_fp8", "smla_sparse_mla_decode_fp8",
            "smla_stage_rows_fp8", "smla_decode_workspace_bytes_mtp", "smla_sparse_mla_decode_mtp",
-           "smla_topk_workspace_bytes", "smla_topk_select")
+           "smla_topk_workspace_bytes", "smla_topk_select", "smla_sparse_mla_decode_noalloc")
 
 
 class SmlaError(RuntimeError):
@@ -92,6 +94,9 @@ def _load() -> ctypes.CDLL:
     lib.smla_topk_workspace_bytes.restype = sz
     lib.smla_topk_select.argtypes = [P, i64, P, i32, i32, P, P, sz, P]
     lib.smla_topk_select.restype = ctypes.c_int
+    lib.smla_sparse_mla_decode_noalloc.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, f32, P,
+                                                   P, P]
+    lib.smla_sparse_mla_decode_noalloc.restype = ctypes.c_int
     return lib
 
 
@@ -237,6 +242,32 @@ def sparse_mla_decode(q: torch.Tensor, cache: torch.Tensor, page_table: torch.Te
     """Sparse MLA decode over cache [P,64,352]; returns (out [B,H,512] fp32, lse [B,H] fp32)."""
     return _decode(q, cache, page_table, seq_lens, topk, softmax_scale, out, lse, workspace,
                    stream, ROW_BYTES, lib.smla_sparse_mla_decode, lib.smla_decode_workspace_bytes)
+
+
+def sparse_mla_decode_noalloc(q: torch.Tensor, cache: torch.Tensor, page_table: torch.Tensor,
+                              seq_lens: torch.Tensor, topk: torch.Tensor, softmax_scale: float,
+                              out: torch.Tensor, lse: torch.Tensor, stream=None):
+    """sparse_mla_decode through the entry point that allocates nothing: the
+    caller passes out [B,H,512] and lse [B,H]; the split partials use the
+    library's static scratch (calls overlapping on one GPU race on it)."""
+    _req(cache, "cache", torch.uint8, 3)
+    dev = cache.device
+    _req(q, "q", torch.bfloat16, 3, dev)
+    _req(page_table, "page_table", torch.int32, 2, dev)
+    _req(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _req(topk, "topk", torch.int32, 2, dev)
+    B, H, D = q.shape
+    if D != DIM or tuple(cache.shape[1:]) != (PAGE_ROWS, ROW_BYTES):
+        raise ValueError("q must be [B,H,576] and cache [num_pages,64,352]")
+    if page_table.shape[0] != B or seq_lens.shape[0] != B or topk.shape[0] != B:
+        raise ValueError("page_table, seq_lens and topk need one row per sequence")
+    _req_shape(out, "out", torch.float32, (B, H, LATENT), dev)
+    _req_shape(lse, "lse", torch.float32, (B, H), dev)
+    _check(lib.smla_sparse_mla_decode_noalloc(
+        q.data_ptr(), cache.data_ptr(), cache.shape[0], page_table.data_ptr(), page_table.shape[1],
+        seq_lens.data_ptr(), topk.data_ptr(), B, H, topk.shape[1], float(softmax_scale),
+        out.data_ptr(), lse.data_ptr(), _stream_ptr(dev, stream)))
+    return out, lse
 
 
 def sparse_mla_decode_fp8(q: torch.Tensor, cache: torch.Tensor, page_table: torch.Tensor,

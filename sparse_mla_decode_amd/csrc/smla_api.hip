@@ -3,6 +3,7 @@
 #include "smla.h"
 #include "smla_internal.h"
 
+#include <mutex>
 #include <string.h>
 
 namespace {
@@ -39,6 +40,9 @@ const char *smla_strerror(int code) {
         case SMLA_ERR_WORKSPACE: return "workspace missing or too small";
         case SMLA_ERR_LAUNCH: return "kernel launch failed";
         case SMLA_ERR_DEVICE: return "no gfx950 device is current";
+        case SMLA_ERR_SCRATCH:
+            return "the shape needs more split-partial scratch than the static no-allocation "
+                   "buffer holds (SMLA_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status code";
     }
 }
@@ -228,3 +232,57 @@ int smla_sparse_mla_decode_mtp(const void *q_bf16, const uint8_t *cache, int64_t
 
 }  // extern "C"
 
+// ---- the decode that allocates nothing ----
+// The split partials of smla_sparse_mla_decode_noalloc live in this static
+// device array (one copy per GPU, each at its own address).  In host code
+// the name `scratch` is only a host-side stand-in: its device address comes
+// from hipGetSymbolAddress, taken once per device with that device current,
+// and only that address is ever handed to a kernel.
+namespace {
+
+__device__ __attribute__((aligned(256))) uint8_t scratch[SMLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices] = {};
+
+// device address of the current device's scratch array (SMLA_OK), looked up
+// on the first call on each device and cached
+int scratch_address(void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SMLA_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return SMLA_ERR_DEVICE;
+        scratch_ptr[dev] = p;
+    }
+    *ptr = scratch_ptr[dev];
+    return SMLA_OK;
+}
+
+}  // namespace
+
+extern "C" int smla_sparse_mla_decode_noalloc(const void *q_bf16, const uint8_t *cache,
+                                              int64_t num_pages, const int32_t *page_table,
+                                              int32_t max_pages, const int32_t *seq_lens,
+                                              const int32_t *topk_indices, int32_t batch,
+                                              int32_t heads, int32_t topk, float softmax_scale,
+                                              float *out, float *lse, void *stream) {
+    const int bad = check_decode_args(q_bf16, cache, num_pages, page_table, max_pages, seq_lens,
+                                      topk_indices, batch, 1, heads, topk, out, lse);
+    if (bad != SMLA_OK) return bad;
+    const size_t need = workspace_bytes(batch, 1, heads, topk, smla::kFmtNvfp4);
+    if (need > SMLA_NOALLOC_SCRATCH_BYTES) return SMLA_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (need > 0) {
+        const int dev = device_ok();
+        if (dev != SMLA_OK) return dev;
+        const int e = scratch_address(&ws);
+        if (e != SMLA_OK) return e;
+    }
+    return decode(q_bf16, cache, num_pages, page_table, max_pages, seq_lens, topk_indices, batch, 1,
+                  heads, topk, softmax_scale, out, lse, ws, SMLA_NOALLOC_SCRATCH_BYTES, stream,
+                  smla::kFmtNvfp4);
+}
