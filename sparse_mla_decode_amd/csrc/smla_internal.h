@@ -26,7 +26,6 @@ constexpr int kMaxBatch = 65535;
 
 // Decode launch plan shared by the host entry points and the kernel.
 struct DecodePlan {
-    bool h64;             // the 64-head kernel (decode_h64.hip): one workgroup per (query, split)
     int heads_per_group;  // 16, 32 or 64: heads one workgroup serves from each row
     int groups;           // heads / heads_per_group
     int splits;           // workgroups sharing one (sequence, head group)
@@ -57,16 +56,6 @@ int64_t topk_workspace_stride(int64_t ld);
 hipError_t launch_topk_select(const float *scores, int64_t ld, const int32_t *seq_lens,
                               int32_t batch, int32_t topk, int32_t *out, uint32_t *ws,
                               hipStream_t stream);
-
-// the 64-head NVFP4 kernel (decode_h64.hip): list entries one split may
-// scan, and the launch of the decode kernel alone (the merge is launched by
-// launch_sparse_mla_decode)
-int h64_max_per_split();
-hipError_t launch_decode_h64(const uint16_t *q, const uint8_t *cache, int64_t num_pages,
-                             const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens,
-                             const int32_t *topk_idx, int32_t batch, int32_t tokens, int32_t topk,
-                             float scale_log2, float *out, float *lse, _Float16 *part_o,
-                             float *part_ml, int32_t splits, int32_t per_split, hipStream_t stream);
 
 hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int64_t num_pages,
                                     const int32_t *page_table, int32_t max_pages,

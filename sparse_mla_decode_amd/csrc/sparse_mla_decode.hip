@@ -910,15 +910,9 @@ __global__ __launch_bounds__(64) void merge_splits_kernel(
 
 }  // namespace
 
-constexpr bool kUseH64 = false;
-
 DecodePlan plan_decode(int batch, int tokens, int heads, int topk, RowFormat fmt) {
     DecodePlan p;
-    // NVFP4 rows at 64 heads may take the kernel of decode_h64.hip, one
-    // workgroup per (query, split) serving all 64 heads; it stays unselected
-    // while it is slower than two head groups of 32 at 64 heads
-    p.h64 = kUseH64 && fmt == kFmtNvfp4 && heads == 64;
-    p.heads_per_group = p.h64 ? 64 : heads >= 32 ? 32 : 16;
+    p.heads_per_group = heads >= 32 ? 32 : 16;
     p.groups = heads / p.heads_per_group;
     const int units = batch * tokens * p.groups;
     const int target = 256;  // one workgroup per CU
@@ -928,8 +922,7 @@ DecodePlan plan_decode(int batch, int tokens, int heads, int topk, RowFormat fmt
     s = s > max_s ? max_s : s;
     s = s > kMaxSplits ? kMaxSplits : s;
     // a split scans at most the row ids its LDS holds
-    const int max_per = p.h64 ? h64_max_per_split()
-                        : fmt == kFmtFp8 ? Ring<kFmtFp8>::kMaxPerSplit : Ring<kFmtNvfp4>::kMaxPerSplit;
+    const int max_per = fmt == kFmtFp8 ? Ring<kFmtFp8>::kMaxPerSplit : Ring<kFmtNvfp4>::kMaxPerSplit;
     const int min_s = (topk + max_per - 1) / max_per;
     s = s < min_s ? min_s : s;
     p.splits = s;
@@ -987,13 +980,6 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
                                             ((o_bytes + 255) & ~(size_t)255));
     }
     const float scale_log2 = (float)((double)scale * 1.4426950408889634074);
-    if (plan.h64) {
-        const hipError_t e = launch_decode_h64(q, cache, num_pages, page_table, max_pages, seq_lens,
-                                               topk_idx, batch, tokens, topk, scale_log2, out, lse,
-                                               part_o, part_ml, plan.splits, plan.per_split, stream);
-        if (e != hipSuccess || plan.splits == 1) return e;
-        return launch_merge(part_o, part_ml, out, lse, heads, plan, batch, tokens, stream);
-    }
 #define SMLA_LAUNCH(MB, FMT)                                                                 \
     hipLaunchKernelGGL((sparse_mla_decode_kernel<MB, FMT>), dim3(blocks), dim3(kThreads), 0, stream, \
                        q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,      \

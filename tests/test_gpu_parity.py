@@ -288,20 +288,13 @@ def _max_moves(scores, splits, slack=8.0):
     return moves
 
 
-# whether the library serves 64-head NVFP4 queries with its 64-head kernel
-H64_KERNEL = False
-
-
 def _plan(batch, heads, topk, fp8=False):
     """Workgroups sharing a list and the split count of the library's plan:
-    with the 64-head kernel, 64-head NVFP4 queries take one workgroup per
-    (query, split) of at most 1024 entries; otherwise head groups of 32 (16)
-    and splits of at most 2048 (FP8: 1024) entries; about 256 workgroups, at
-    most 16 splits."""
-    h64 = H64_KERNEL and heads == 64 and not fp8
-    units = batch * (1 if h64 else max(1, heads // 32))
+    head groups of 32 (16) and splits of at most 2048 (FP8: 1024) entries;
+    about 256 workgroups, at most 16 splits."""
+    units = batch * max(1, heads // 32)
     splits = max(1, min(-(-256 // units), -(-topk // 64), 16))
-    cap = 1024 if (h64 or fp8) else 2048
+    cap = 1024 if fp8 else 2048
     return units, max(splits, -(-topk // cap))
 
 
@@ -338,13 +331,12 @@ def test_decode_running_max_moves(dev, smla, batch, heads):
 
 
 def test_decode_64_heads_long_splits(dev, smla):
-    """128 queries of 64 heads: one split per workgroup (two of 1024 entries
-    with the 64-head kernel, one of 2048 with head groups), sixteen or more
-    tiles per workgroup, so the tile pipeline runs long; every query and head
-    against the oracle."""
+    """128 queries of 64 heads: 256 workgroups of one split of 2048 entries,
+    32 tiles per workgroup, so the tile pipeline runs long and no merge
+    follows; every query and head against the oracle."""
     note("decode B=128 H=64 K=2048 (long splits)")
     case = _shared_pages_case(128, 64, 40, 2048, seed=88)
-    assert _plan(128, 64, 2048) == ((128, 2) if H64_KERNEL else (256, 1))
+    assert _plan(128, 64, 2048) == (256, 1)
     cache_d = gpu_cache(case, dev, smla)
     cache_o = oracle_cache(case)
     out, lse = gpu_decode(case, cache_d, dev, smla)
