@@ -13,9 +13,10 @@ roofline of the decode kernel, cpu_baseline of the oracle on host cores).
 `--path staged` replaces the fused decode by the staged path (gather-unpack
 of the NVFP4 rows into a lean FP8 copy in HBM, then the FP8 decode over it).
 `--op select` times the top-k select over the workload's synthetic indexer
-scores instead, and `--op mtp --tokens T` a multi-token step (T new rows
-appended per sequence, then T queries per sequence, each with its own list);
-each prints its own JSON line.
+scores instead, `--op mtp --tokens T` a multi-token step (T new rows
+appended per sequence, then T queries per sequence, each with its own list),
+and `--op append` the bulk quantise-append of the workload's tail rows (the
+ragged and million configurations); each prints its own JSON line.
 """
 from __future__ import annotations
 
@@ -48,22 +49,43 @@ def log(msg):
     sys.stderr.flush()
 
 
-def kernel_source_hash() -> str:
-    """First 16 hex digits of the sha256 of the decode kernels' source file."""
+# the sources each kernel family is compiled from (its .hip file and the
+# device headers it includes)
+KERNEL_SOURCES = {
+    "decode": ("sparse_mla_decode.hip", "decode_device.h"),
+    "append": ("kv_quant_append.hip",),
+    "select": ("topk_select.hip",),
+    "staged": ("stage_rows.hip",),
+}
+
+
+def source_hash(kind: str = "decode") -> str:
+    """First 16 hex digits of the sha256 over a kernel family's source files."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "sparse_mla_decode_amd", "csrc", "sparse_mla_decode.hip"), "rb") as f:
-        h.update(f.read())
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "sparse_mla_decode_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def kernel_source_hash() -> str:
+    """The decode kernels' source hash (the key of the traffic record)."""
+    return source_hash("decode")
+
+
+def source_hashes() -> dict:
+    return {k: source_hash(k) for k in KERNEL_SOURCES}
 
 
 def traffic_key(workload: str, fmt: str) -> str:
     return workload if fmt == "nvfp4" else workload + "-" + fmt
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, full: bool = False):
     """HBM bytes per decode call from committed rocprofv3 counter runs, or None
     when the kernel source changed since they were taken.  The file holds one
-    line per workload: `<workload> <source hash> <bytes per call> ...`."""
+    line per workload: `<workload> <source hash> <bytes per call> <fetch>
+    <write>`; with full=True the (total, fetch, write) triple."""
     try:
         with open(TRAFFIC_FILE) as f:
             lines = f.read().splitlines()
@@ -71,10 +93,10 @@ def measured_traffic(workload: str):
         return None
     for ln in lines:
         parts = ln.split()
-        if len(parts) >= 3 and parts[0] == workload and not ln.startswith("#"):
+        if len(parts) >= 5 and parts[0] == workload and not ln.startswith("#"):
             if parts[1] != kernel_source_hash():
                 return None
-            return int(parts[2])
+            return (int(parts[2]), int(parts[3]), int(parts[4])) if full else int(parts[2])
     return None
 
 
@@ -93,7 +115,8 @@ def summarize_kernel_stats(d):
     library's kernels (and the total of one decode call)."""
     rows = _csv_rows(d, "kernel_stats.csv")
     import re
-    out = ["%-60s %8s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
+    out = ["# source hashes: " + " ".join("%s=%s" % kv for kv in source_hashes().items()),
+           "%-60s %8s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
     for r in rows:
         name = r["Name"]
         if "smla" not in name:
@@ -182,6 +205,43 @@ def events_ms(fn, n):
     return e0.elapsed_time(e1) / n
 
 
+COPY_BYTES = 1 << 30             # stream-copy denominator: 1 GiB read + 1 GiB written
+FLUSH_BYTES = 1 << 30            # scratch written between launches in the flush cross-check
+
+
+def stream_copy_gbps(dev, reps: int = 20) -> float:
+    """HBM bandwidth of a plain device copy measured on this GPU: 1 GiB copied
+    reps times back to back, read + written bytes over the HIP-event time."""
+    import torch
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    ms = events_ms(lambda i: b.copy_(a), reps)
+    del a, b
+    return 2 * COPY_BYTES / (ms * 1e-3) / 1e9
+
+
+def flushed_median_us(fn, n: int, dev) -> float:
+    """Median per-launch time (us) of fn(i) when 1 GiB of scratch is written
+    before each launch, so that nothing a launch reads or writes is left in
+    the L2s or the Infinity Cache by the launches before it.  Each launch is
+    bracketed by its own pair of HIP events."""
+    import torch
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(evs):
+        scratch.zero_()
+        e0.record()
+        fn(i)
+        e1.record()
+    torch.cuda.synchronize()
+    del scratch
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+
+
 def summarize_pmc(dirs):
     """Per-kernel averages per dispatch of the counters in one or more
     rocprofv3 --pmc directories, and what they imply.  GRBM_GUI_ACTIVE as
@@ -224,14 +284,25 @@ def summarize_pmc(dirs):
     return "\n".join(out)
 
 
+HOST_SHARE = 16                  # host cores that go with one GPU on the measurement hosts
+
+
+def host_threads():
+    """(threads for the oracle, cores in this process's affinity): all
+    affinity cores, but at most one GPU's share of the host (16), so that a
+    one-GPU run does not oversubscribe the cores that belong to the other
+    GPUs of the host."""
+    aff = len(os.sched_getaffinity(0))
+    return min(aff, HOST_SHARE), aff
+
+
 def cpu_baseline(w, seed, lens, tk_np, qbits, budget_s, dev, fmt):
     """Time the oracle's decode on host cores over as many sequences as fit in
     roughly budget_s seconds (at least one)."""
     import torch
     import oracle
     import workloads as wl
-    cores = len(os.sched_getaffinity(0))
-    cores = min(cores, 16)
+    cores, aff = host_threads()
     done, t_used, kv_bytes = 0, 0.0, 0
     order = list(range(w.batch))
     for b in order:
@@ -254,11 +325,11 @@ def cpu_baseline(w, seed, lens, tk_np, qbits, budget_s, dev, fmt):
         if t_used >= budget_s:
             break
     gbps = kv_bytes / t_used / 1e9
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": "oracle decode (fp64 C, OpenMP over heads) of %d of %d sequences "
-                      "(%d heads, %d selected rows each), %.1f s; %.2f queries/s"
-                      % (done, w.batch, w.heads, int(np.mean([min(w.topk, L) for L in lens])),
-                         t_used, done / t_used)}
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": min(cores, w.heads), "kind": "oracle",
+            "sample": "oracle decode (fp64 C, OpenMP over heads, %d threads of %d affinity cores) "
+                      "of %d of %d sequences (%d heads, %d selected rows each), %.1f s; %.2f queries/s"
+                      % (cores, aff, done, w.batch, w.heads,
+                         int(np.mean([min(w.topk, L) for L in lens])), t_used, done / t_used)}
 
 
 def bench_select(args, w, dev):
@@ -301,6 +372,7 @@ def bench_select(args, w, dev):
         "config": {"workload": w.name, "batch": w.batch, "topk": w.topk,
                    "scores_per_query": int(first.shape[1]), "rotating_sets": sets},
         "select_us": round(us, 2), "queries_per_s": round(w.batch / (us * 1e-6), 1),
+        "source_hashes": source_hashes(),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
     }
@@ -386,6 +458,7 @@ def bench_mtp(args, w, dev):
         "unique_rows_frac": round(uniq_bytes / dec_bytes, 4),
         "decode_tflops": round(tflops, 2),
         "queries_per_s": round(w.batch * T / (ms * 1e-3), 1),
+        "source_hashes": source_hashes(),
         "roofline": ({"bound": "hbm", "achieved": round(uniq_bytes / dec_s / 1e9, 1),
                       "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                       "frac": round(uniq_bytes / dec_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None}
@@ -398,7 +471,7 @@ def bench_mtp(args, w, dev):
         import oracle
         tk0 = tks[0].cpu().numpy()
         qb = wl.bf16_bits(qs[0])
-        cores = min(len(os.sched_getaffinity(0)), 16)
+        cores, aff = host_threads()
         t_used, done, kvb = 0.0, 0, 0
         for b in range(w.batch):
             sel_all = [tk0[b, j][tk0[b, j] >= 0].astype(np.int64) for j in range(T)]
@@ -423,9 +496,83 @@ def bench_mtp(args, w, dev):
             if t_used >= args.cpu_budget:
                 break
         result["cpu_baseline"] = {
-            "value": round(kvb / t_used / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": "oracle multi-token decode (fp64 C, OpenMP over heads) of %d of %d "
-                      "sequences x %d tokens, %.1f s" % (done, w.batch, T, t_used)}
+            "value": round(kvb / t_used / 1e9, 4), "unit": "GB/s", "cores": min(cores, w.heads),
+            "kind": "oracle",
+            "sample": "oracle multi-token decode (fp64 C, OpenMP over heads, %d threads of %d "
+                      "affinity cores) of %d of %d sequences x %d tokens, %.1f s"
+                      % (cores, aff, done, w.batch, T, t_used)}
+    print(json.dumps(result), flush=True)
+
+
+def bench_append(args, w, dev):
+    """The bulk quantise-append of the workload's tail: the newest
+    min(tail, L) tokens of every sequence (ragged, million) or the newest
+    token (other workloads), into their cache slots.  Algorithmic bytes: a
+    BF16 row read (1,152 B) and a cache row written per row."""
+    import torch
+    import sparse_mla_decode_amd as smla
+    import workloads as wl
+    fmt = args.format
+    rb = ROW_BYTES[fmt]
+    lens = wl.context_lengths(w, args.seed)
+    pt_np, num_pages = wl.build_page_table(w, lens, args.seed)
+    cache = torch.zeros((num_pages, 64, rb), dtype=torch.uint8, device=dev)
+    tail = w.append_tail if w.append_tail else 1
+    rows, slots = wl.tail_rows(w, args.seed, lens, pt_np, dev, tail)
+    fn = smla.kv_quant_append if fmt == "nvfp4" else smla.kv_quant_append_fp8
+    n = rows.shape[0]
+    per_row = 576 * 2 + rb
+    log("append %s (%s rows): %d rows, %.1f MB per call" % (w.name, fmt, n, n * per_row / 1e6))
+    call = lambda i: fn(rows, slots, cache)
+    warm_clocks(call, args.warm_seconds)
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = events_ms(call, args.steps)
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the same slots rewritten after a 1 GiB scratch write: no row of the
+    # previous call still sits in the Infinity Cache
+    flush_us = flushed_median_us(call, min(args.steps, 50), dev)
+    copy_gbps = stream_copy_gbps(dev)
+    gbps = n * per_row / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "quantise-append of BF16 KV rows into the paged %s cache: GB/s (%% HBM peak) "
+                  "and rows/sec" % ("NVFP4" if fmt == "nvfp4" else "lean FP8"),
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "warm_seconds": args.warm_seconds, "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "row_format": fmt, "rows": int(n), "bytes_per_row": per_row,
+                   "desc": w.desc},
+        "append_us": round(ms * 1e3, 2),
+        "append_us_flushed_median": round(flush_us, 2),
+        "append_GBps_flushed": round(n * per_row / (flush_us * 1e-6) / 1e9, 1),
+        "rows_per_s": round(n / (ms * 1e-3), 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "stream_copy_GBps": round(copy_gbps, 1),
+        "frac_of_copy": round(gbps / copy_gbps, 4),
+        "source_hashes": source_hashes(),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+    }
+    if not args.no_cpu:
+        import oracle
+        quant = oracle.quant_rows if fmt == "nvfp4" else oracle.quant_rows_fp8
+        bits = wl.bf16_bits(rows)          # host copy, outside the timed region
+        chunk = 4096
+        t_used, done = 0.0, 0
+        while done < n and t_used < args.cpu_budget:
+            part = np.ascontiguousarray(bits[done:done + chunk])
+            t = time.perf_counter()
+            quant(part)
+            t_used += time.perf_counter() - t
+            done += part.shape[0]
+        result["cpu_baseline"] = {
+            "value": round(done * per_row / t_used / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "oracle quant_rows (scalar C, one thread) of %d of %d rows, %.1f s; "
+                      "%.0f rows/s" % (done, n, t_used, done / t_used)}
     print(json.dumps(result), flush=True)
 
 
@@ -439,8 +586,9 @@ def main():
     ap.add_argument("--workload", default="allheads")
     ap.add_argument("--format", choices=("nvfp4", "fp8"), default="nvfp4",
                     help="cache row format: NVFP4 (352 B) or lean FP8 (576 B)")
-    ap.add_argument("--op", choices=("decode", "select", "mtp"), default="decode",
-                    help="the decode step (default), the top-k select alone, or an MTP step")
+    ap.add_argument("--op", choices=("decode", "select", "mtp", "append"), default="decode",
+                    help="the decode step (default), the top-k select alone, an MTP step, or "
+                         "the bulk append of the workload's tail rows")
     ap.add_argument("--tokens", type=int, default=4, help="query tokens per sequence (--op mtp)")
     ap.add_argument("--path", choices=("fused", "staged"), default="fused",
                     help="decode path: the fused kernel, or the staged ablation (NVFP4 only)")
@@ -486,6 +634,9 @@ def main():
         return
     if args.op == "mtp":
         bench_mtp(args, w, dev)
+        return
+    if args.op == "append":
+        bench_append(args, w, dev)
         return
     fmt = args.format
     if args.path == "staged" and fmt != "nvfp4":
@@ -584,7 +735,19 @@ def main():
     dec_tflops = dec_flops / dec_s / 1e12
     ai = w.heads * FLOPS_PER_HEAD_ROW / rbytes
     ridge = MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    traffic = measured_traffic(traffic_key(w.name, fmt) + ("-staged" if args.path == "staged" else ""))
+    tkey = traffic_key(w.name, fmt) + ("-staged" if args.path == "staged" else "")
+    traffic = measured_traffic(tkey)
+    traffic_full = measured_traffic(tkey, full=True)
+    # a plain copy's bandwidth on this GPU (the second denominator), and the
+    # flush cross-check of the call time
+    copy_gbps = stream_copy_gbps(dev)
+    flush_us = flushed_median_us(decode_call, min(args.steps, 100), dev)
+    # all bytes a decode call moves at least once: the selected rows, q, the
+    # lists, one page-table entry per valid entry, seq_lens, out and lse, and
+    # the split partials written then read back by the merge
+    nv_mean = float(np.mean([nvalid[s] for s in used]))
+    all_bytes = (dec_bytes + w.batch * w.heads * 576 * 2 + w.batch * w.topk * 4 + nv_mean * 4
+                 + w.batch * 4 + w.batch * w.heads * (512 + 1) * 4 + 2 * ws_bytes)
     if ai >= ridge:
         roof = {"bound": "mfma", "achieved": round(dec_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(dec_tflops / MFMA_F16_PEAK_TFLOPS, 4),
@@ -620,6 +783,13 @@ def main():
         "decode_tflops": round(dec_tflops, 2),
         "append_us": round(float(app_ms.mean()) * 1e3, 2),
         "gpu_us_per_step": round(gpu_step_ms * 1e3, 2),
+        "decode_us_flushed_median": round(flush_us, 2),
+        "stream_copy_GBps": round(copy_gbps, 1),
+        "decode_kv_frac_of_copy": round(dec_gbps / copy_gbps, 4),
+        "decode_all_bytes": int(all_bytes),
+        "decode_all_GBps": round(all_bytes / dec_s / 1e9, 1),
+        "overfetch": (round(traffic_full[1] / dec_bytes, 3) if traffic_full else None),
+        "source_hashes": source_hashes(),
         "roofline": roof,
     }
     if not args.no_cpu:
