@@ -344,6 +344,48 @@ def test_decode_64_heads_long_splits(dev, smla):
     check_parity(out, ref_o, lse, ref_l)
 
 
+def test_split_partials_f16_error_share(dev, smla):
+    """A split stores its normalised partial in f16 (one rounding after the
+    fp32 accumulation).  8 queries of 64 heads take 16 splits of 128 entries.
+    The oracle decodes each split's slice of the list exactly; merging those
+    exact partials reproduces the oracle's decode (which pins the split
+    boundaries), and merging their f16 roundings gives the result an exact
+    kernel with f16 partials would return.  Its distance from the exact
+    decode is the partials' error, bounded per element by 2^-11 times the
+    largest partial magnitude; its share of the GPU's error is reported."""
+    B, H, K = 8, 64, 2048
+    note("decode B=%d H=%d K=%d: f16 partials' error share" % (B, H, K))
+    case = small_case(B, H, [4096] * B, K, seed=77)
+    units, splits = _plan(B, H, K)
+    assert splits == 16
+    per = -(-K // splits)
+    cache_o = oracle_cache(case)
+    cache_d = gpu_cache(case, dev, smla)
+    out, lse = gpu_decode(case, cache_d, dev, smla)
+    ref_o, ref_l = oracle_decode(case, cache_o)
+    parts = []
+    for sp in range(splits):
+        cs = dict(case)
+        cs["topk"] = np.ascontiguousarray(case["topk"][:, sp * per:(sp + 1) * per])
+        parts.append(oracle_decode(cs, cache_o))
+    po = np.stack([p[0] for p in parts])          # [S, B, H, 512] normalised partials
+    pl = np.stack([p[1] for p in parts])          # [S, B, H] natural-log sums
+    w = np.exp(pl - np.logaddexp.reduce(pl, axis=0))[..., None]   # split weights, sum 1
+    exact = (w * po).sum(0)
+    rounded = (w * po.astype(np.float16).astype(np.float64)).sum(0)
+    assert rel_l2(exact, ref_o) < 1e-12
+    # |f16(x) - x| <= 2^-11 |x| (2^-25 below f16's normal range); the weights
+    # are a convex combination
+    bound = 2.0 ** -11 * np.abs(po).max(0) + 2.0 ** -24
+    assert (np.abs(rounded - exact) <= bound).all()
+    e_part, e_gpu = rel_l2(rounded, ref_o), rel_l2(out, ref_o)
+    note("  f16 partials rel_l2 %.3e, GPU rel_l2 %.3e: share %.2f" % (e_part, e_gpu, e_part / e_gpu))
+    check_parity(out, ref_o, lse, ref_l)
+    # the partials' rounding is one rounding among the path's f16 roundings
+    # (operands, weights): it cannot exceed the bar by itself
+    assert e_part <= OUT_TOL / 10
+
+
 # --------------------------------------------------------------------------
 # full-size workloads: all queries on the GPU, sampled sequences on the oracle
 # --------------------------------------------------------------------------
