@@ -531,7 +531,8 @@ def test_decode_workspace_reuse_across_shapes(dev, smla):
     note("decode workspace reuse across shapes")
     from cases import gpu_cache, small_case
     shapes = [(2, 64, [5000, 1500], 2048), (1, 16, [4096], 256), (4, 16, [2500, 2500, 90, 700], 2048),
-              (5, 64, [2100, 300, 64, 1, 4000], 2048), (1, 64, [70000], 2048), (3, 16, [3000, 777, 64], 512)]
+              (5, 64, [2100, 300, 64, 1, 4000], 2048), (1, 64, [70000], 2048), (3, 16, [3000, 777, 64], 512),
+              (128, 16, [3000] * 128, 2048)]
     need = max(max(smla.decode_workspace_bytes(b, h, k), smla.decode_workspace_bytes_fp8(b, h, k))
                for b, h, _, k in shapes)
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
