@@ -100,6 +100,8 @@ def _load():
     lib.oracle_fp8_row_bytes.restype = ctypes.c_int
     lib.oracle_row_bytes.restype = ctypes.c_int
     lib.oracle_page_rows.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -147,6 +149,13 @@ def e2m1_nearest(x, S) -> np.ndarray:
 
 
 # -- rows ---------------------------------------------------------------
+
+def set_threads(nthreads: int) -> int:
+    """Thread count of the row quantisers' OpenMP loops for later calls from
+    this thread (timing only; the results do not depend on it).  Returns the
+    count they will use."""
+    return int(_load().oracle_set_threads(int(nthreads)))
+
 
 def quant_rows(rows_bf16_bits: np.ndarray) -> np.ndarray:
     """[n,576] uint16 (BF16 bit patterns) -> [n,352] uint8 NVFP4 rows."""

@@ -206,6 +206,22 @@ void oracle_quant_row(const uint16_t *x, uint8_t *row)
         row[ROPE_OFF + j] = oracle_e4m3_nearest(bf16_value(x[LATENT + j]), 1.0);
 }
 
+/* Timing infrastructure, no arithmetic: the thread count of the OpenMP
+ * loops that take none as an argument (the row quantisers) for later calls
+ * from the calling thread; nthreads <= 0 keeps the current one.  Returns the
+ * count those loops will use (1 without OpenMP). */
+int oracle_set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+    return omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
 /* One 352-byte row -> its 576 exact values: latent d is
  * e2m1(nibble d) * E4M3(scale of block d/16), rope j is E4M3(byte j). */
 void oracle_dequant_row(const uint8_t *row, double *k)
