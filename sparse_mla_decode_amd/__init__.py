@@ -111,8 +111,16 @@ def _check(code: int):
         raise SmlaError(code, lib)
 
 
+# torch's raw current-stream query: the same pointer as
+# torch.cuda.current_stream(device).cuda_stream without building a Stream
+# object (0.07 us against 2 us per call, a large share of a call's host time)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_ptr(device: torch.device, stream=None) -> int:
     if stream is None:
+        if _raw_stream is not None and device.index is not None:
+            return int(_raw_stream(device.index))
         stream = torch.cuda.current_stream(device)
     return int(stream.cuda_stream)
 

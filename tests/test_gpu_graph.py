@@ -28,6 +28,18 @@ def smla():
     return m
 
 
+def test_stream_pointer_follows_current_stream(dev, smla):
+    """The binding launches on torch's current stream: the default one, and a
+    side stream made current by torch.cuda.stream."""
+    assert smla._stream_ptr(dev) == torch.cuda.current_stream(dev).cuda_stream
+    s = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(s):
+        assert smla._stream_ptr(dev) == s.cuda_stream
+        assert smla._stream_ptr(dev) == torch.cuda.current_stream(dev).cuda_stream
+    assert smla._stream_ptr(dev) == torch.cuda.current_stream(dev).cuda_stream
+    assert smla._stream_ptr(dev, s) == s.cuda_stream
+
+
 def test_graph_replays_equal_eager(dev, smla):
     note("graph capture of append + decode and select + decode")
     w = wl.WORKLOADS["tp4"]
