@@ -10,7 +10,7 @@
 // Radix select over an order-preserving 32-bit key of each fp32 score, in
 // three digits (bits 31..21, 20..10, 9..0).  Two passes read every score:
 //   pass 0: histogram of digit 0 over the query's L scores (workgroups of
-//           4096 scores, 8192 for long rows: LDS histogram, then the
+//           2048 to 16384 scores by row length: LDS histogram, then the
 //           non-empty bins added to the query's histogram with global
 //           atomics);
 //   pass 1: every workgroup finds, from that histogram, the bin b0 holding
@@ -37,10 +37,13 @@
 namespace smla {
 namespace {
 
-// Scores per workgroup of the two full passes, and its threads: 4096 and
-// 256, or, for rows of 256K scores or more, 8192 and 512 (fewer workgroups
-// adding into each query's histogram).  Every thread loads 4 float4.
-constexpr int kPer = 4;
+// Scores per workgroup of the two full passes (threads x loads per thread x
+// 4): rows under 64K scores take 2048 (256 threads, 2 float4 each), so that
+// short rows still spread over many workgroups; rows under 256K take 4096
+// (256 x 4); longer rows take 16384 (512 x 8), so that fewer workgroups add
+// into each query's histogram.  Every thread has all its loads in flight
+// before it uses any.
+constexpr int64_t kMidRow = 65536;
 constexpr int64_t kBigRow = 262144;
 constexpr int kFinThreads = 1024;
 constexpr int kBins0 = 2048, kBins1 = 2048, kBins2 = 1024;
@@ -117,7 +120,7 @@ __device__ void find_bin(const uint32_t *hist, uint32_t k, uint32_t *scan_lds, u
 }
 
 // Pass 0: histogram of digit 0.
-template <int kThreads>
+template <int kThreads, int kPer>
 __global__ __launch_bounds__(kThreads) void topk_hist_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ seq_lens,
     int32_t topk, int32_t chunks, uint32_t *__restrict__ ws, int64_t ws_stride) {
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(
 }
 
 // Pass 1: keys above bin b0 to the list, keys in b0 to the candidates.
-template <int kThreads>
+template <int kThreads, int kPer>
 __global__ __launch_bounds__(kThreads) void topk_split_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ seq_lens,
     int32_t topk, int32_t chunks, uint32_t *__restrict__ ws, int64_t ws_stride, int64_t cap,
@@ -347,18 +350,19 @@ hipError_t launch_topk_select(const float *scores, int64_t ld, const int32_t *se
                               hipStream_t stream) {
     const int64_t stride = topk_workspace_stride(ld);
     const int64_t cap = topk_candidate_cap(ld);
-#define SMLA_PASSES(NT)                                                                        \
+#define SMLA_PASSES(NT, PER)                                                                   \
     do {                                                                                       \
-        const int64_t ch = 4 * kPer * (NT);                                                    \
+        const int64_t ch = 4 * (PER) * (NT);                                                   \
         const int32_t chunks = (int32_t)((ld + ch - 1) / ch);                                  \
         const dim3 grid((unsigned)((int64_t)batch * chunks)), block(NT);                       \
-        hipLaunchKernelGGL(topk_hist_kernel<NT>, grid, block, 0, stream, scores, ld, seq_lens,  \
-                           topk, chunks, ws, stride);                                          \
-        hipLaunchKernelGGL(topk_split_kernel<NT>, grid, block, 0, stream, scores, ld, seq_lens, \
-                           topk, chunks, ws, stride, cap, out);                                \
+        hipLaunchKernelGGL((topk_hist_kernel<NT, PER>), grid, block, 0, stream, scores, ld,    \
+                           seq_lens, topk, chunks, ws, stride);                                \
+        hipLaunchKernelGGL((topk_split_kernel<NT, PER>), grid, block, 0, stream, scores, ld,   \
+                           seq_lens, topk, chunks, ws, stride, cap, out);                      \
     } while (0)
-    if (ld >= kBigRow) SMLA_PASSES(512);
-    else SMLA_PASSES(256);
+    if (ld >= kBigRow) SMLA_PASSES(512, 8);
+    else if (ld >= kMidRow) SMLA_PASSES(256, 4);
+    else SMLA_PASSES(256, 2);
 #undef SMLA_PASSES
     hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)batch), dim3(kFinThreads), 0, stream,
                        scores, ld, seq_lens, topk, ws, stride, cap, out);

@@ -53,7 +53,7 @@ def run(smla, dev, scores: np.ndarray, lens: np.ndarray, K: int):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("ld", [20000, 300000])  # the second takes the 8192-score workgroups
+@pytest.mark.parametrize("ld", [20000, 100000, 300000])  # workgroups of 2048, 4096, 16384 scores
 def test_select_random_rows_and_lengths(dev, smla, ld):
     note("topk random rows ld=%d" % ld)
     rng = np.random.default_rng(1)
