@@ -245,7 +245,6 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
     __shared__ uint32_t scan_lds[kFinThreads];
     __shared__ uint32_t res_lds[2];
     __shared__ uint32_t place_lds[2];
-    __shared__ uint2 cand_lds[kMaxCand];
     const int64_t b = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t L = min((int64_t)max(seq_lens[b], 0), ld);
@@ -262,41 +261,40 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
     const int64_t n_src = in_buf ? (int64_t)n_c : L;
     const uint2 *cand = reinterpret_cast<const uint2 *>(q + kCand);
     const float *row = scores + b * ld;
-    if (in_buf) {  // all loads in flight at once, then LDS only
-        constexpr int kLoads = kMaxCand / kFinThreads;  // 16
-        uint2 v[kLoads];
+    const int lane = tid & 63;
+    // This thread's candidates, i = tid + kFinThreads k: held in registers
+    // for all three passes when the buffer holds them all (every load in
+    // flight at once), else read from the scores in each pass.
+    constexpr int kLoads = kMaxCand / kFinThreads;  // 16
+    uint2 v[kLoads];
+    if (in_buf) {
 #pragma unroll
         for (int k = 0; k < kLoads; ++k) {
             const int64_t i = tid + (int64_t)kFinThreads * k;
             if (i < n_src) v[k] = cand[i];
         }
-#pragma unroll
-        for (int k = 0; k < kLoads; ++k) {
-            const int64_t i = tid + (int64_t)kFinThreads * k;
-            if (i < n_src) cand_lds[i] = v[k];
-        }
-        __syncthreads();
     }
-    // candidate i: (key, position); from the scores, a key outside b0 is no candidate
-    auto get = [&](int64_t i, uint32_t &key, uint32_t &pos) -> bool {
+    // fn(key, pos) for each of this thread's candidates (from the scores, a
+    // key outside bin b0 is no candidate)
+    auto each = [&](auto fn) {
         if (in_buf) {
-            const uint2 v = cand_lds[i];
-            key = v.x;
-            pos = v.y;
-            return true;
+#pragma unroll
+            for (int k = 0; k < kLoads; ++k) {
+                if ((int64_t)kFinThreads * k >= n_src) break;
+                if (tid + (int64_t)kFinThreads * k < n_src) fn(v[k].x, v[k].y);
+            }
+        } else {
+            for (int64_t i = tid; i < n_src; i += kFinThreads) {
+                const uint32_t key = score_key(row[i]);
+                if ((key >> 21) == b0) fn(key, (uint32_t)i);
+            }
         }
-        key = score_key(row[i]);
-        pos = (uint32_t)i;
-        return (key >> 21) == b0;
     };
     const uint32_t need = (uint32_t)topk - a0;
     // digit 1
     for (int i = tid; i < kBins1; i += kFinThreads) h[i] = 0u;
     __syncthreads();
-    for (int64_t i = tid; i < n_src; i += kFinThreads) {
-        uint32_t key, pos;
-        if (get(i, key, pos)) atomicAdd(&h[(key >> 10) & 2047u], 1u);
-    }
+    each([&](uint32_t key, uint32_t) { atomicAdd(&h[(key >> 10) & 2047u], 1u); });
     __syncthreads();
     uint32_t b1, a1;
     find_bin<kBins1, kFinThreads>(h, need, scan_lds, res_lds, b1, a1);
@@ -304,10 +302,9 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
     for (int i = tid; i < kBins2; i += kFinThreads) h[i] = 0u;
     __syncthreads();
     const uint32_t p01 = (b0 << 11) | b1;
-    for (int64_t i = tid; i < n_src; i += kFinThreads) {
-        uint32_t key, pos;
-        if (get(i, key, pos) && (key >> 10) == p01) atomicAdd(&h[key & 1023u], 1u);
-    }
+    each([&](uint32_t key, uint32_t) {
+        if ((key >> 10) == p01) atomicAdd(&h[key & 1023u], 1u);
+    });
     __syncthreads();
     uint32_t b2, a2;
     find_bin<kBins2, kFinThreads>(h, need - min(a1, need - 1), scan_lds, res_lds, b2, a2);
@@ -316,15 +313,45 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
     const uint32_t need_eq = (uint32_t)topk - n_gt;
     if (tid < 2) place_lds[tid] = 0u;
     __syncthreads();
-    for (int64_t i = tid; i < n_src; i += kFinThreads) {
-        uint32_t key, pos;
-        if (!get(i, key, pos)) continue;
-        if (key > T) {
-            const uint32_t pl = a0 + atomicAdd(&place_lds[0], 1u);
+    // the keys above T after the a0 written by the split pass, then the first
+    // need_eq keys equal to T: one LDS atomic per wave and kind reserves the
+    // places of all its lanes (in lane order); called by every lane of a wave
+    const uint64_t below = (1ull << lane) - 1ull;  // the lanes under this one
+    auto place = [&](bool gt, bool eq, uint32_t pos) {
+        const uint64_t mg = __ballot(gt), me = __ballot(eq);
+        if ((mg | me) == 0) return;
+        uint32_t bg = 0, be = 0;
+        if (lane == 0) {
+            if (mg) bg = atomicAdd(&place_lds[0], (uint32_t)__popcll(mg));
+            if (me) be = atomicAdd(&place_lds[1], (uint32_t)__popcll(me));
+        }
+        bg = __shfl(bg, 0, 64);
+        be = __shfl(be, 0, 64);
+        if (gt) {
+            const uint32_t pl = a0 + bg + (uint32_t)__popcll(mg & below);
             if (pl < n_gt) o[pl] = (int32_t)pos;
-        } else if (key == T) {
-            const uint32_t e = atomicAdd(&place_lds[1], 1u);
+        } else if (eq) {
+            const uint32_t e = be + (uint32_t)__popcll(me & below);
             if (e < need_eq) o[n_gt + e] = (int32_t)pos;
+        }
+    };
+    if (in_buf) {
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) {
+            if ((int64_t)kFinThreads * k >= n_src) break;
+            const bool ok = tid + (int64_t)kFinThreads * k < n_src;
+            place(ok && v[k].x > T, ok && v[k].x == T, v[k].y);
+        }
+    } else {
+        for (int64_t i0 = 0; i0 < n_src; i0 += kFinThreads) {  // the same trip count in every lane
+            const int64_t i = i0 + tid;
+            uint32_t key = 0u;
+            bool ok = false;
+            if (i < n_src) {
+                key = score_key(row[i]);
+                ok = (key >> 21) == b0;
+            }
+            place(ok && key > T, ok && key == T, (uint32_t)i);
         }
     }
     // leave the query's workspace all zero: hist0, state, counts and the
