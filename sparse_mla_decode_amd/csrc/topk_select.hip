@@ -49,7 +49,7 @@ constexpr int kFinThreads = 1024;
 constexpr int kBins0 = 2048, kBins1 = 2048, kBins2 = 1024;
 constexpr int kHist0 = 0;
 constexpr int kState = kHist0 + kBins0;
-constexpr int kCount = kState + 4;
+constexpr int kCount = kState + 4;    // 8-byte aligned: one 64-bit counter pair
 constexpr int kCand = kCount + 4;     // candidate pairs start here (8-byte aligned)
 constexpr int64_t kMaxCand = 16384;   // candidates the finish keeps in LDS (128 KB)
 
@@ -208,9 +208,16 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(
     }
     const uint32_t n_gt_t = __popc(gt_mask), n_in_t = __popc(in_mask);
     const uint32_t incl = block_scan<kThreads>(n_gt_t | (n_in_t << 16), scan_lds);
-    if (tid == kThreads - 1) {
-        base_lds[0] = (incl & 0xFFFFu) ? atomicAdd(&q[kCount + 0], incl & 0xFFFFu) : 0u;
-        base_lds[1] = (incl >> 16) ? atomicAdd(&q[kCount + 1], incl >> 16) : 0u;
+    if (tid == kThreads - 1 && incl != 0u) {
+        // both counts in one 64-bit atomic (list places in the low word,
+        // candidates in the high one): one request on the query's counters
+        // per workgroup
+        const unsigned long long add =
+            (unsigned long long)(incl & 0xFFFFu) | ((unsigned long long)(incl >> 16) << 32);
+        const unsigned long long old =
+            atomicAdd(reinterpret_cast<unsigned long long *>(&q[kCount]), add);
+        base_lds[0] = (uint32_t)old;
+        base_lds[1] = (uint32_t)(old >> 32);
     }
     __syncthreads();
     uint32_t pg = base_lds[0] + (incl & 0xFFFFu) - n_gt_t;
