@@ -223,17 +223,19 @@ def stream_copy_gbps(dev, reps: int = 20) -> float:
 
 
 def flushed_median_us(fn, n: int, dev) -> float:
-    """Median per-launch time (us) of fn(i) when 1 GiB of scratch is written
+    """Median per-launch time (us) of fn(i) when 1 GiB of scratch is read
     before each launch, so that nothing a launch reads or writes is left in
-    the L2s or the Infinity Cache by the launches before it.  Each launch is
-    bracketed by its own pair of HIP events."""
+    the L2s or the Infinity Cache by the launches before it.  A read, not a
+    write: a written flush leaves dirty lines whose write-back would fall
+    inside the timed launch.  Each launch is bracketed by its own pair of
+    HIP events."""
     import torch
-    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n)]
     torch.cuda.synchronize()
     for i, (e0, e1) in enumerate(evs):
-        scratch.zero_()
+        scratch.sum()
         e0.record()
         fn(i)
         e1.record()
