@@ -83,23 +83,29 @@ __device__ uint32_t block_scan(uint32_t v, uint32_t *scan_lds) {
 // number of keys in the bins above it.  Thread t of NT owns bins
 // [NB - (t+1) NB/NT, NB - t NB/NT), so thread 0 holds the top ones.  With
 // fewer than k keys in the histogram the answer is (0, 0).
+// The thread's bins of find_bin, highest first (loaded separately so that a
+// caller can issue these loads before others it does not wait for yet).
 template <int NB, int NT>
-__device__ void find_bin(const uint32_t *hist, uint32_t k, uint32_t *scan_lds, uint32_t *res_lds,
-                         uint32_t &bin, uint32_t &above) {
+__device__ __forceinline__ void load_bins(const uint32_t *hist, uint32_t (&h)[NB / NT]) {
+    constexpr int per = NB / NT;
+    const int top = NB - (int)threadIdx.x * per;  // one past this thread's highest bin
+#pragma unroll
+    for (int i = 0; i < per; ++i) h[i] = hist[top - 1 - i];
+}
+
+template <int NB, int NT>
+__device__ void find_bin_of(const uint32_t (&h)[NB / NT], uint32_t k, uint32_t *scan_lds,
+                            uint32_t *res_lds, uint32_t &bin, uint32_t &above) {
     constexpr int per = NB / NT;
     const int tid = threadIdx.x;
     const int top = NB - tid * per;  // one past this thread's highest bin
-    uint32_t h[per];
     uint32_t sum = 0;
     if (tid == 0) {
         res_lds[0] = 0u;
         res_lds[1] = 0u;
     }
 #pragma unroll
-    for (int i = 0; i < per; ++i) {
-        h[i] = hist[top - 1 - i];
-        sum += h[i];
-    }
+    for (int i = 0; i < per; ++i) sum += h[i];
     const uint32_t before = block_scan<NT>(sum, scan_lds) - sum;
     if (before < k && k <= before + sum) {
         uint32_t cum = before;
@@ -117,6 +123,14 @@ __device__ void find_bin(const uint32_t *hist, uint32_t k, uint32_t *scan_lds, u
     bin = res_lds[0];
     above = res_lds[1];
     __syncthreads();
+}
+
+template <int NB, int NT>
+__device__ void find_bin(const uint32_t *hist, uint32_t k, uint32_t *scan_lds, uint32_t *res_lds,
+                         uint32_t &bin, uint32_t &above) {
+    uint32_t h[NB / NT];
+    load_bins<NB, NT>(hist, h);
+    find_bin_of<NB, NT>(h, k, scan_lds, res_lds, bin, above);
 }
 
 // Pass 0: histogram of digit 0.
@@ -178,14 +192,19 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(
     if (begin >= L) return;
     uint32_t *q = ws + b * ws_stride;
     const float *row = scores + b * ld;
-    float4 v[kPer];  // the chunk's loads in flight while the threshold bin is found
+    // the thread's histogram bins first, then the chunk's scores: loads
+    // complete in order, so the scores stay in flight while the threshold
+    // bin is found
+    uint32_t hb[kBins0 / kThreads];
+    load_bins<kBins0, kThreads>(q + kHist0, hb);
+    float4 v[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int64_t i0 = begin + 4 * (int64_t)(tid + kThreads * k);
         v[k] = *reinterpret_cast<const float4 *>(row + min(i0, ld - 4));  // in the row; masked below
     }
     uint32_t b0, a0;
-    find_bin<kBins0, kThreads>(q + kHist0, (uint32_t)topk, scan_lds, res_lds, b0, a0);
+    find_bin_of<kBins0, kThreads>(hb, (uint32_t)topk, scan_lds, res_lds, b0, a0);
     if (c == 0 && tid == 0) {
         q[kState + 0] = b0;
         q[kState + 1] = a0;
