@@ -54,7 +54,7 @@ def log(msg):
 KERNEL_SOURCES = {
     "decode": ("sparse_mla_decode.hip", "decode_device.h"),
     "append": ("kv_quant_append.hip",),
-    "select": ("topk_select.hip",),
+    "select": ("topk_select.hip", "decode_device.h"),
     "staged": ("stage_rows.hip",),
 }
 

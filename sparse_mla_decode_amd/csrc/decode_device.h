@@ -1,7 +1,7 @@
-// Device helpers shared by the decode kernels: vector types, the NVFP4 tile
+// Device helpers shared by the kernels: vector types, the NVFP4 tile
 // swizzle, exact format converters (e2m1 / E4M3 -> f16 through the gfx950
-// scaled converters, BF16 -> f16), DPP row reductions, and the direct-to-LDS
-// row load with its explicit wait.  Row format: "Prime Inference: serving
+// scaled converters, BF16 -> f16), DPP row reductions and wave prefix sums,
+// and the direct-to-LDS row load with its explicit wait.  Row format: "Prime Inference: serving
 // GLM-5.3 to agents is a KV-cache problem", section "Four bits per latent
 // value: where 352 comes from".
 #pragma once
@@ -47,6 +47,28 @@ __device__ __forceinline__ half8_t join4(half4_t a, half4_t b) {
     r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
     r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
     return r;
+}
+
+// v plus the value of the lane the DPP control names (0 where it names none);
+// ROWS masks the 16-lane rows that take the sum (the others keep v)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t add_dpp(uint32_t v) {
+    return v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+// Inclusive prefix over the 64 lanes of a wave, in registers: row shifts by
+// 1, 2, 4 and 8 give each 16-lane row its own prefix; then rows 1 and 3 add
+// lane 15 of the row before, and rows 2 and 3 add lane 31 (the row
+// broadcasts of this chip's DPP).  Lane shuffles would make each of the six
+// steps an LDS permute round trip.
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v) {
+    v = add_dpp<0x111, 0xF>(v);  // row_shr:1
+    v = add_dpp<0x112, 0xF>(v);  // row_shr:2
+    v = add_dpp<0x114, 0xF>(v);  // row_shr:4
+    v = add_dpp<0x118, 0xF>(v);  // row_shr:8
+    v = add_dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = add_dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
 }
 
 // Reductions over the 16 lanes of a row with DPP lane moves (quad swaps,

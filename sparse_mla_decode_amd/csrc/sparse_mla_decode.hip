@@ -544,12 +544,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
             cnt_valid += rid[i] != 0xFFFFFFFFu;
         }
         // inclusive scan of the counts within the wave (list order preserved)
-        incl = cnt_valid;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int v = __shfl_up(incl, d, 64);
-            if (lane >= d) incl += v;
-        }
+        incl = (int)wave_scan_dpp((uint32_t)cnt_valid);
         if (lane == 63) scan_lds[wave - 4] = incl;
     }
     __syncthreads();

@@ -32,6 +32,7 @@
 // and position).  It must be zero before its first use; the finish clears
 // every word of its query that the call wrote, so each call leaves the
 // workspace all zero, ready for a call of any shape.
+#include "decode_device.h"
 #include "smla_internal.h"
 
 namespace smla {
@@ -59,33 +60,13 @@ __device__ __forceinline__ uint32_t score_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// v plus the value of the lane the DPP control names (0 where it names none)
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t add_dpp(uint32_t v) {
-    return v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
-}
-
-// Inclusive prefix over the 64 lanes of a wave in registers: row shifts by
-// 1, 2, 4 and 8 give each 16-lane row its own prefix; then row 1 and row 3
-// add lane 15 of the row before, and rows 2 and 3 add lane 31 (row
-// broadcasts, which this chip's DPP has).  No LDS round trip.
-__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v) {
-    v = add_dpp<0x111, 0xF>(v);  // row_shr:1
-    v = add_dpp<0x112, 0xF>(v);  // row_shr:2
-    v = add_dpp<0x114, 0xF>(v);  // row_shr:4
-    v = add_dpp<0x118, 0xF>(v);  // row_shr:8
-    v = add_dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-    v = add_dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-    return v;
-}
-
 // Inclusive prefix over the threads of a workgroup (NT threads): within each
 // wave in registers, then the wave totals through LDS (two barriers).
 template <int NT>
 __device__ uint32_t block_scan(uint32_t v, uint32_t *scan_lds) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    v = wave_scan_dpp(v);
+    v = dev::wave_scan_dpp(v);
     if (lane == 63) scan_lds[wave] = v;
     __syncthreads();
     uint32_t off = 0;
