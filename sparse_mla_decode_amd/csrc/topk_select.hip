@@ -268,6 +268,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
     __shared__ uint32_t scan_lds[kFinThreads];
     __shared__ uint32_t res_lds[2];
     __shared__ uint32_t place_lds[2];
+    __shared__ uint32_t sel_lds[64];
     const int64_t b = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t L = min((int64_t)max(seq_lens[b], 0), ld);
@@ -321,17 +322,58 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
     __syncthreads();
     uint32_t b1, a1;
     find_bin<kBins1, kFinThreads>(h, need, scan_lds, res_lds, b1, a1);
-    // digit 2 among the keys with digits (b0, b1)
-    for (int i = tid; i < kBins2; i += kFinThreads) h[i] = 0u;
-    __syncthreads();
+    // digit 2 among the keys with digits (b0, b1): the threshold key T is
+    // the need2-th largest of them, a2 the number above it.  Usually they are
+    // a handful, which one wave ranks directly; more (heavily tied data)
+    // take a histogram of digit 2.
     const uint32_t p01 = (b0 << 11) | b1;
-    each([&](uint32_t key, uint32_t) {
-        if ((key >> 10) == p01) atomicAdd(&h[key & 1023u], 1u);
-    });
-    __syncthreads();
-    uint32_t b2, a2;
-    find_bin<kBins2, kFinThreads>(h, need - min(a1, need - 1), scan_lds, res_lds, b2, a2);
-    const uint32_t T = (p01 << 10) | b2;
+    const uint32_t need2 = need - min(a1, need - 1);
+    const uint32_t n1 = h[b1];  // their number, from the digit-1 histogram
+    uint32_t T, a2;
+    if (n1 <= 64) {
+        if (tid == 0) place_lds[0] = 0u;
+        __syncthreads();
+        each([&](uint32_t key, uint32_t) {
+            if ((key >> 10) == p01) {
+                const uint32_t e = atomicAdd(&place_lds[0], 1u);
+                if (e < 64) sel_lds[e] = key;
+            }
+        });
+        __syncthreads();
+        if (tid < 64) {
+            const uint32_t n = min(place_lds[0], 64u);  // n1 for a consistent workspace
+            const uint32_t mine = (uint32_t)tid < n ? sel_lds[tid] : 0u;
+            uint32_t gt = 0, ge = 0;  // keys above this lane's, and at or above it
+            for (uint32_t j = 0; j < n; ++j) {
+                const uint32_t kj = __builtin_amdgcn_readlane(mine, j);
+                gt += kj > mine;
+                ge += kj >= mine;
+            }
+            const uint64_t hit = __ballot((uint32_t)tid < n && gt < need2 && need2 <= ge);
+            if (hit != 0 && tid == (int)__builtin_ctzll(hit)) {
+                res_lds[0] = mine;
+                res_lds[1] = gt;
+            } else if (hit == 0 && tid == 0) {  // an inconsistent workspace only
+                res_lds[0] = p01 << 10;
+                res_lds[1] = 0u;
+            }
+        }
+        __syncthreads();
+        T = res_lds[0];
+        a2 = res_lds[1];
+        __syncthreads();  // before place_lds and res_lds are used again
+    } else {
+        __syncthreads();  // every thread has read n1 from h
+        for (int i = tid; i < kBins2; i += kFinThreads) h[i] = 0u;
+        __syncthreads();
+        each([&](uint32_t key, uint32_t) {
+            if ((key >> 10) == p01) atomicAdd(&h[key & 1023u], 1u);
+        });
+        __syncthreads();
+        uint32_t b2;
+        find_bin<kBins2, kFinThreads>(h, need2, scan_lds, res_lds, b2, a2);
+        T = (p01 << 10) | b2;
+    }
     const uint32_t n_gt = min(a0 + a1 + a2, (uint32_t)topk - 1);  // keys above T
     const uint32_t need_eq = (uint32_t)topk - n_gt;
     if (tid < 2) place_lds[tid] = 0u;
@@ -348,8 +390,8 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
             if (mg) bg = atomicAdd(&place_lds[0], (uint32_t)__popcll(mg));
             if (me) be = atomicAdd(&place_lds[1], (uint32_t)__popcll(me));
         }
-        bg = __shfl(bg, 0, 64);
-        be = __shfl(be, 0, 64);
+        bg = __builtin_amdgcn_readfirstlane(bg);  // lane 0's reservations (every lane is active)
+        be = __builtin_amdgcn_readfirstlane(be);
         if (gt) {
             const uint32_t pl = a0 + bg + (uint32_t)__popcll(mg & below);
             if (pl < n_gt) o[pl] = (int32_t)pos;
