@@ -16,12 +16,13 @@
 //   pass 1: every workgroup finds, from that histogram, the bin b0 holding
 //           the K-th largest key and the count a0 of keys above it; keys
 //           above b0 go straight to the list (one atomic per workgroup
-//           reserves their places), keys in b0 are appended to the query's
-//           candidate buffer;
-//   finish: one workgroup per query loads the candidates into LDS and
-//           selects the remaining K - a0 keys among them (digits 1 and 2,
-//           then the keys above the threshold key T and the first of those
-//           equal to it).
+//           reserves their places and the candidates' slots), keys in b0
+//           are appended to the query's candidate buffer;
+//   finish: one workgroup per query loads the candidates into registers
+//           and selects the remaining K - a0 keys among them (digit 1, then
+//           digit 2 -- by one wave when few keys share the first two
+//           digits -- then the keys above the threshold key T and the
+//           first of those equal to it).
 // When bin b0 holds more keys than the candidate buffer, the finish reads
 // them from the scores instead (correct, slower; only for heavily tied data).
 // Which of several equal scores at the threshold are taken, and the order of
@@ -52,7 +53,7 @@ constexpr int kHist0 = 0;
 constexpr int kState = kHist0 + kBins0;
 constexpr int kCount = kState + 4;    // 8-byte aligned: one 64-bit counter pair
 constexpr int kCand = kCount + 4;     // candidate pairs start here (8-byte aligned)
-constexpr int64_t kMaxCand = 16384;   // candidates the finish keeps in LDS (128 KB)
+constexpr int64_t kMaxCand = 16384;   // candidates the finish holds (16 per thread, in registers)
 
 // Larger key <=> larger score (finite scores; -0 sorts just below +0).
 __device__ __forceinline__ uint32_t score_key(float x) {
@@ -76,12 +77,10 @@ __device__ uint32_t block_scan(uint32_t v, uint32_t *scan_lds) {
     return v + off;
 }
 
-// The bin of hist[0..NB) holding the k-th largest key (k >= 1), and the
-// number of keys in the bins above it.  Thread t of NT owns bins
-// [NB - (t+1) NB/NT, NB - t NB/NT), so thread 0 holds the top ones.  With
-// fewer than k keys in the histogram the answer is (0, 0).
-// The thread's bins of find_bin, highest first (loaded separately so that a
-// caller can issue these loads before others it does not wait for yet).
+// Thread t of NT owns bins [NB - (t+1) NB/NT, NB - t NB/NT) of a histogram,
+// so thread 0 holds the top ones.  Its bins, highest first (loaded apart
+// from find_bin_of so that a caller can issue these loads before others it
+// does not wait for yet):
 template <int NB, int NT>
 __device__ __forceinline__ void load_bins(const uint32_t *hist, uint32_t (&h)[NB / NT]) {
     constexpr int per = NB / NT;
@@ -90,6 +89,9 @@ __device__ __forceinline__ void load_bins(const uint32_t *hist, uint32_t (&h)[NB
     for (int i = 0; i < per; ++i) h[i] = hist[top - 1 - i];
 }
 
+// The bin of hist[0..NB) holding the k-th largest key (k >= 1), and the
+// number of keys in the bins above it, from every thread's bins.  With fewer
+// than k keys in the histogram the answer is (0, 0).
 template <int NB, int NT>
 __device__ void find_bin_of(const uint32_t (&h)[NB / NT], uint32_t k, uint32_t *scan_lds,
                             uint32_t *res_lds, uint32_t &bin, uint32_t &above) {
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ seq_lens,
     int32_t topk, int32_t chunks, uint32_t *__restrict__ ws, int64_t ws_stride, int64_t cap,
     int32_t *__restrict__ out) {
-    __shared__ uint32_t scan_lds[kThreads];
+    __shared__ uint32_t scan_lds[kThreads / 64];  // a wave total each
     __shared__ uint32_t res_lds[2];
     __shared__ uint32_t base_lds[2];
     const int64_t b = blockIdx.x / chunks;
@@ -258,14 +260,15 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(
 }
 
 // Finish: one workgroup per query selects the last K - a0 keys among the
-// candidates (all in bin b0): digit 1, then digit 2, then the keys above
+// candidates (all in bin b0): digit 1, then digit 2 (one wave ranks the
+// keys sharing the first two digits when they are few), then the keys above
 // the threshold key and the first equal ones.
 __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ seq_lens,
     int32_t topk, uint32_t *__restrict__ ws, int64_t ws_stride, int64_t cap,
     int32_t *__restrict__ out) {
     __shared__ uint32_t h[kBins1];
-    __shared__ uint32_t scan_lds[kFinThreads];
+    __shared__ uint32_t scan_lds[kFinThreads / 64];  // a wave total each
     __shared__ uint32_t res_lds[2];
     __shared__ uint32_t place_lds[2];
     __shared__ uint32_t sel_lds[64];
