@@ -63,6 +63,27 @@ def test_select_random_rows_and_lengths(dev, smla, ld):
     check_lists(got, x, lens, 2048, exact_sets=True)
 
 
+@pytest.mark.parametrize("group", [1, 2, 63, 64, 65, 200])
+def test_select_threshold_group_sizes(dev, smla, group):
+    """The keys that share the threshold's first two radix digits (the top
+    22 bits of the key) number `group`: up to 64 of them one wave ranks, more
+    take a digit-2 histogram.  They are distinct floats 1 + 5k ulp (one
+    digit-1 bin of the digit-0 bin of 1.0); 40 larger scores sit above them
+    and the threshold falls inside the group."""
+    note("topk threshold group of %d keys" % group)
+    rng = np.random.default_rng(10 + group)
+    L, K = 4096, 40 + max(1, group - 3)
+    x = -1000.0 - rng.random(L).astype(np.float32) * 100  # far below
+    x[:40] = 100.0 + np.arange(40, dtype=np.float32)
+    bits = (0x3F800000 + 5 * np.arange(group)).astype(np.uint32)
+    x[40:40 + group] = bits.view(np.float32)
+    x = x[rng.permutation(L)].astype(np.float32)
+    rows = np.stack([x, np.roll(x, 7)])
+    lens = np.array([L, L - 1], dtype=np.int64)
+    got = run(smla, dev, rows, lens, K)
+    check_lists(got, rows, lens, K, exact_sets=True)
+
+
 @pytest.mark.parametrize("K", [1, 17, 256, 2048])
 def test_select_ties_at_the_threshold(dev, smla, K):
     note("topk ties K=%d" % K)
