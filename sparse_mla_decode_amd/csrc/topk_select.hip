@@ -62,8 +62,10 @@ __device__ __forceinline__ uint32_t score_key(float x) {
 }
 
 // Inclusive prefix over the threads of a workgroup (NT threads): within each
-// wave in registers, then the wave totals through LDS (two barriers).
-template <int NT>
+// wave in registers, then the wave totals through LDS.  REUSE: a second
+// barrier lets the caller write scan_lds again afterwards (without it, each
+// scan needs an array of its own).
+template <int NT, bool REUSE = true>
 __device__ uint32_t block_scan(uint32_t v, uint32_t *scan_lds) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -73,7 +75,7 @@ __device__ uint32_t block_scan(uint32_t v, uint32_t *scan_lds) {
     uint32_t off = 0;
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) off += w < wave ? scan_lds[w] : 0u;
-    __syncthreads();
+    if constexpr (REUSE) __syncthreads();
     return v + off;
 }
 
@@ -91,8 +93,9 @@ __device__ __forceinline__ void load_bins(const uint32_t *hist, uint32_t (&h)[NB
 
 // The bin of hist[0..NB) holding the k-th largest key (k >= 1), and the
 // number of keys in the bins above it, from every thread's bins.  With fewer
-// than k keys in the histogram the answer is (0, 0).
-template <int NB, int NT>
+// than k keys in the histogram the answer is (0, 0).  REUSE: scan_lds and
+// res_lds may be written again afterwards (two more barriers).
+template <int NB, int NT, bool REUSE = true>
 __device__ void find_bin_of(const uint32_t (&h)[NB / NT], uint32_t k, uint32_t *scan_lds,
                             uint32_t *res_lds, uint32_t &bin, uint32_t &above) {
     constexpr int per = NB / NT;
@@ -105,7 +108,7 @@ __device__ void find_bin_of(const uint32_t (&h)[NB / NT], uint32_t k, uint32_t *
     }
 #pragma unroll
     for (int i = 0; i < per; ++i) sum += h[i];
-    const uint32_t before = block_scan<NT>(sum, scan_lds) - sum;
+    const uint32_t before = block_scan<NT, REUSE>(sum, scan_lds) - sum;
     if (before < k && k <= before + sum) {
         uint32_t cum = before;
 #pragma unroll
@@ -121,7 +124,7 @@ __device__ void find_bin_of(const uint32_t (&h)[NB / NT], uint32_t k, uint32_t *
     __syncthreads();
     bin = res_lds[0];
     above = res_lds[1];
-    __syncthreads();
+    if constexpr (REUSE) __syncthreads();
 }
 
 template <int NB, int NT>
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ seq_lens,
     int32_t topk, int32_t chunks, uint32_t *__restrict__ ws, int64_t ws_stride, int64_t cap,
     int32_t *__restrict__ out) {
-    __shared__ uint32_t scan_lds[kThreads / 64];  // a wave total each
+    __shared__ uint32_t scan_a[kThreads / 64], scan_b[kThreads / 64];  // a wave total each
     __shared__ uint32_t res_lds[2];
     __shared__ uint32_t base_lds[2];
     const int64_t b = blockIdx.x / chunks;
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(
         v[k] = *reinterpret_cast<const float4 *>(row + min(i0, ld - 4));  // in the row; masked below
     }
     uint32_t b0, a0;
-    find_bin_of<kBins0, kThreads>(hb, (uint32_t)topk, scan_lds, res_lds, b0, a0);
+    find_bin_of<kBins0, kThreads, false>(hb, (uint32_t)topk, scan_a, res_lds, b0, a0);
     if (c == 0 && tid == 0) {
         q[kState + 0] = b0;
         q[kState + 1] = a0;
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(
         }
     }
     const uint32_t n_gt_t = __popc(gt_mask), n_in_t = __popc(in_mask);
-    const uint32_t incl = block_scan<kThreads>(n_gt_t | (n_in_t << 16), scan_lds);
+    const uint32_t incl = block_scan<kThreads, false>(n_gt_t | (n_in_t << 16), scan_b);
     if (tid == kThreads - 1 && incl != 0u) {
         // both counts in one 64-bit atomic (list places in the low word,
         // candidates in the high one): one request on the query's counters
