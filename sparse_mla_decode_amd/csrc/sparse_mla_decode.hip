@@ -546,10 +546,35 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         // inclusive scan of the counts within the wave (list order preserved)
         incl = (int)wave_scan_dpp((uint32_t)cnt_valid);
         if (lane == 63) scan_lds[wave - 4] = incl;
+        // Tile 0 as the compaction will write it if every one of the split's
+        // first 64 entries is usable (entries a shorter split does not have
+        // are padding rows, id 0).  Written now, its loads can go out right
+        // after this barrier, before the compaction; scan_lds[4] says whether
+        // it holds.  Those entries all lie in the first value wave.
+        const int n_entries = e_end - e_begin;
+        bool bad = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int p = vt * per_thread + i;
+            if (i < per_thread && p < kTile) {
+                const bool absent = p >= n_entries;
+                bad |= !absent && rid[i] == 0xFFFFFFFFu;
+                rowid_lds[p] = (absent || rid[i] == 0xFFFFFFFFu) ? 0u : rid[i];
+            }
+        }
+        if (wave == 4) {
+            const bool any_bad = __ballot(bad) != 0;
+            if (lane == 0) scan_lds[4] = any_bad ? 0 : 1;
+        }
     }
     __syncthreads();
     const int n_valid = count_valid();
     const int n_tiles = (n_valid + kTile - 1) / kTile;
+    // tile 0 is already in rowid_lds as the compaction writes it again: its
+    // loads go out now (the compaction's stores of the same ids meanwhile
+    // change nothing those loads read)
+    const bool early0 = n_tiles > 0 && __builtin_amdgcn_readfirstlane(scan_lds[4]) != 0;
+    if (early0) issue(0);
     // the last tile is padded with row 0 of page 0 (always in the cache): the
     // loads then need no per-row guard, and the padding rows get zero weight
     const int n_pad = n_tiles * kTile;
@@ -675,7 +700,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     // of tile 0.
     // Tile t + 1 is complete one barrier before the score waves read it at
     // the end of step t: before F0 for t = 0, before B(t) after that
-    for (int T = 0; T <= 1 && T < n_tiles; ++T) issue(T);
+    for (int T = early0 ? 1 : 0; T <= 1 && T < n_tiles; ++T) issue(T);
     if (n_tiles > 0) wait_tile(min(1, n_tiles - 1));
     __syncthreads();
     uint32_t rk[kMaxDma];  // row ids of the next tile to load
