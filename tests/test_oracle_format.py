@@ -165,6 +165,56 @@ def test_e2m1_encode_brute_force_every_scale():
     assert checked > 2_000_000
 
 
+def _rocm_host_e2m1(tmpdir):
+    """ROCm's software float -> e2m1 conversion (tests/hip_fp4_ref.cpp),
+    built with hipcc, host code only; None without hipcc."""
+    import ctypes
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        return None
+    src = os.path.join(os.path.dirname(__file__), "hip_fp4_ref.cpp")
+    so = os.path.join(str(tmpdir), "libhip_fp4_ref.so")
+    r = subprocess.run([hipcc, "-std=c++17", "-O1", "-fPIC", "-shared", "-x", "hip", "--offload-host-only",
+                        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", src, "-o", so],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lib = ctypes.CDLL(so)
+    lib.hip_host_e2m1.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+
+    def conv(x):
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.zeros(x.size, dtype=np.uint8)
+        lib.hip_host_e2m1(x.ctypes.data, x.size, out.ctypes.data)
+        return out
+    return conv
+
+
+def test_e2m1_encode_matches_rocm_host_reference(tmp_path):
+    """The e2m1 rounding against a library routine: ROCm's software OCP FP4
+    conversion (round to nearest even, saturating at 6) at block scale 1,
+    and at power-of-two scales S, where x / S is exact.  Inputs: every
+    multiple of 1/64 in [-10, 10] (all tie points among them), the floats
+    next to each tie point, signed zeros, subnormals, saturating values and
+    10^5 normal draws."""
+    conv = _rocm_host_e2m1(tmp_path)
+    if conv is None:
+        pytest.skip("hipcc not found")
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+    x = np.concatenate([
+        np.arange(-640, 641, dtype=np.float32) / np.float32(64.0),
+        np.array([0.0, -0.0, 1e-40, -1e-40, 6.0001, 5.9999, 1e30, -1e30], dtype=np.float32),
+        np.nextafter(mids, np.float32(10.0)), np.nextafter(mids, np.float32(-10.0)),
+        -np.nextafter(mids, np.float32(10.0)), -mids,
+        np.random.default_rng(7).normal(0.0, 3.0, 100_000).astype(np.float32)])
+    want = conv(x)
+    assert np.array_equal(oracle.e2m1_nearest(x.astype(np.float64), 1.0), want)
+    for k in (-6, -2, 3, 8):
+        S = 2.0 ** k
+        assert np.array_equal(oracle.e2m1_nearest(x.astype(np.float64) * S, S), want), k
+
+
 def test_e2m1_tie_points():
     S = 1.0
     mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
