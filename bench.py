@@ -166,7 +166,8 @@ def summarize_counters(fetch_dir, write_dir, workload):
     for c, (f, dk, mk, n) in res.items():
         lines.append("# %-10s %.4f %14.1f %14.1f %6d" % (c, f, dk, mk, n))
     lines.append("# workload  source_hash  hbm_bytes_per_call  fetch_bytes  write_bytes")
-    lines.append("%s %s %d %d %d" % (workload, kernel_source_hash(), int(fb + wb), int(fb), int(wb)))
+    fb, wb = int(fb), int(wb)  # the total is the sum of the recorded parts
+    lines.append("%s %s %d %d %d" % (workload, kernel_source_hash(), fb + wb, fb, wb))
     return "\n".join(lines)
 
 
