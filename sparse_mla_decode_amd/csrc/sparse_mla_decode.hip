@@ -62,6 +62,7 @@ constexpr int kSStride = kTile + 8;             // f16 per scale-table row (144 
 constexpr int kKSteps = kDim / 32;              // 18 score steps of 32
 constexpr float kSlack = 8.0f;                  // log2 headroom before the running max moves
 constexpr int kMaxSplits = 16;
+constexpr int kCusPerXcd = 32;                   // 8 XCDs x 32 CUs
 
 // The tile ring for each row format: row bytes, where the rope bytes start,
 // ring slots, and how far ahead the loads run (tile s + kAhead is loaded in
@@ -930,21 +931,51 @@ __global__ __launch_bounds__(64) void merge_splits_kernel(
 
 }  // namespace
 
-DecodePlan plan_decode(int batch, int tokens, int heads, int topk, RowFormat fmt) {
-    DecodePlan p;
-    p.heads_per_group = heads >= 32 ? 32 : 16;
-    p.groups = heads / p.heads_per_group;
-    const int units = batch * tokens * p.groups;
-    const int target = 256;  // one workgroup per CU
-    int s = (target + units - 1) / units;
+namespace {
+
+// Splits per unit for head groups of `hg` heads.  A workgroup holds a CU,
+// and the workgroups of sequence sq all run on XCD sq % 8 (32 CUs): the
+// launch stays within one wave of workgroups when the busiest XCD's share
+// of them fits its CUs.  At most one split per 64-row tile, at most
+// kMaxSplits, and at least as many as the row-id table of a split needs.
+int plan_splits(int batch, int tokens, int heads, int hg, int topk, RowFormat fmt) {
+    const int seqs_per_xcd = (batch + 7) / 8;
+    const int wg_per_split = seqs_per_xcd * tokens * (heads / hg);
+    int s = kCusPerXcd / wg_per_split;
     const int max_s = (topk + kTile - 1) / kTile;
     s = s < 1 ? 1 : s;
     s = s > max_s ? max_s : s;
     s = s > kMaxSplits ? kMaxSplits : s;
-    // a split scans at most the row ids its LDS holds
     const int max_per = fmt == kFmtFp8 ? Ring<kFmtFp8>::kMaxPerSplit : Ring<kFmtNvfp4>::kMaxPerSplit;
     const int min_s = (topk + max_per - 1) / max_per;
-    s = s < min_s ? min_s : s;
+    return s < min_s ? min_s : s;
+}
+
+int tiles_per_split(int topk, int splits) {
+    const int per = (topk + splits - 1) / splits;
+    return (per + kTile - 1) / kTile;
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int batch, int tokens, int heads, int topk, RowFormat fmt) {
+    DecodePlan p;
+    p.heads_per_group = heads >= 32 ? 32 : 16;
+    int s = plan_splits(batch, tokens, heads, p.heads_per_group, topk, fmt);
+    if (heads == 64) {
+        // 16-head groups unpack every row twice as often as 32-head ones;
+        // they pay when 32-head groups leave splits of at most two tiles
+        // (the per-workgroup start dominates) and 16-head groups give as
+        // many workgroups, each with more tiles (fewer splits to merge)
+        const int s16 = plan_splits(batch, tokens, heads, 16, topk, fmt);
+        const int t32 = tiles_per_split(topk, s), t16 = tiles_per_split(topk, s16);
+        if (t32 <= 2 && t16 > t32 && 4 * s16 >= 2 * s) {
+            p.heads_per_group = 16;
+            s = s16;
+        }
+    }
+    p.groups = heads / p.heads_per_group;
+    const int units = batch * tokens * p.groups;
     p.splits = s;
     p.per_split = (topk + s - 1) / s;
     p.partial_bytes = (size_t)p.heads_per_group * kLatent * sizeof(_Float16) +

@@ -288,14 +288,30 @@ def _max_moves(scores, splits, slack=8.0):
     return moves
 
 
-def _plan(batch, heads, topk, fp8=False):
-    """Workgroups sharing a list and the split count of the library's plan:
-    head groups of 32 (16) and splits of at most 2048 (FP8: 1024) entries;
-    about 256 workgroups, at most 16 splits."""
-    units = batch * max(1, heads // 32)
-    splits = max(1, min(-(-256 // units), -(-topk // 64), 16))
+def _plan(batch, heads, topk, fp8=False, tokens=1):
+    """Workgroups sharing a list, and the split count, of the library's plan.
+    Splits: as many as keep the busiest XCD (32 CUs; sequence s runs on XCD
+    s % 8) at one workgroup per CU, at most 16, at most one per 64-row tile,
+    and of at most 2048 (FP8: 1024) entries.  Head groups: 32 heads (16 at 16
+    heads), or 16 at 64 heads where 32-head groups would leave splits of at
+    most two tiles and 16-head groups give as many workgroups with more."""
     cap = 1024 if fp8 else 2048
-    return units, max(splits, -(-topk // cap))
+
+    def splits(hg):
+        s = max(1, 32 // (-(-batch // 8) * tokens * (heads // hg)))
+        s = min(s, -(-topk // 64), 16)
+        return max(s, -(-topk // cap))
+
+    def tiles(s):
+        return -(-(-(-topk // s)) // 64)
+
+    hg = 32 if heads >= 32 else 16
+    s = splits(hg)
+    if heads == 64:
+        s16 = splits(16)
+        if tiles(s) <= 2 and tiles(s16) > tiles(s) and 4 * s16 >= 2 * s:
+            hg, s = 16, s16
+    return batch * tokens * (heads // hg), s
 
 
 def _shared_pages_case(batch, heads, pages, topk, seed):
@@ -346,18 +362,19 @@ def test_decode_64_heads_long_splits(dev, smla):
 
 def test_split_partials_f16_error_share(dev, smla):
     """A split stores its normalised partial in f16 (one rounding after the
-    fp32 accumulation).  8 queries of 64 heads take 16 splits of 128 entries.
+    fp32 accumulation).
     The oracle decodes each split's slice of the list exactly; merging those
     exact partials reproduces the oracle's decode (which pins the split
     boundaries), and merging their f16 roundings gives the result an exact
     kernel with f16 partials would return.  Its distance from the exact
     decode is the partials' error, bounded per element by 2^-11 times the
-    largest partial magnitude; its share of the GPU's error is reported."""
+    largest partial magnitude; its share of the GPU's error is reported.
+    (8 queries of 64 heads take 16-head groups and 8 splits of 256.)"""
     B, H, K = 8, 64, 2048
     note("decode B=%d H=%d K=%d: f16 partials' error share" % (B, H, K))
     case = small_case(B, H, [4096] * B, K, seed=77)
     units, splits = _plan(B, H, K)
-    assert splits == 16
+    assert (units, splits) == (32, 8)
     per = -(-K // splits)
     cache_o = oracle_cache(case)
     cache_d = gpu_cache(case, dev, smla)
