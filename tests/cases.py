@@ -148,3 +148,30 @@ def gpu_decode(case, cache_dev, dev, smla):
 def oracle_decode(case, cache_np):
     return oracle.sparse_mla_decode(case["q"], cache_np, case["pt"], case["lens"], case["topk"],
                                     case["scale"])
+
+
+def decode_plan(batch, heads, topk, fp8=False, tokens=1):
+    """(workgroups sharing a list, splits, heads per group) of the library's
+    plan, restated from its rule.
+    Splits: as many as keep the busiest XCD (32 CUs; sequence s runs on XCD
+    s % 8) at one workgroup per CU, at most 16, at most one per 64-row tile,
+    and of at most 2048 (FP8: 1024) entries.  Head groups: 32 heads (16 at 16
+    heads), or 16 at 64 heads where 32-head groups would leave splits of at
+    most two tiles and 16-head groups give as many workgroups with more."""
+    cap = 1024 if fp8 else 2048
+
+    def splits(hg):
+        s = max(1, 32 // (-(-batch // 8) * tokens * (heads // hg)))
+        s = min(s, -(-topk // 64), 16)
+        return max(s, -(-topk // cap))
+
+    def tiles(s):
+        return -(-(-(-topk // s)) // 64)
+
+    hg = 32 if heads >= 32 else 16
+    s = splits(hg)
+    if heads == 64:
+        s16 = splits(16)
+        if tiles(s) <= 2 and tiles(s16) > tiles(s) and 4 * s16 >= 2 * s:
+            hg, s = 16, s16
+    return batch * tokens * (heads // hg), s, hg

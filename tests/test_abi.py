@@ -49,6 +49,37 @@ def test_workspace_sizes():
     assert smla.decode_workspace_bytes(1, 16, 64) == 0
 
 
+def test_workspace_sizes_follow_the_plan():
+    """The split plan, restated in tests/cases.py (and used there to choose
+    shapes that reach given split counts), against the library: the
+    workspace a call needs is that plan's f16 partials and fp32 (m, l),
+    each 256-byte rounded, or nothing for one split."""
+    import sparse_mla_decode_amd as smla
+    from cases import decode_plan
+
+    def expect(batch, heads, topk, fp8=False, tokens=1):
+        units, s, hg = decode_plan(batch, heads, topk, fp8, tokens)
+        if s == 1:
+            return 0
+        r = lambda x: (x + 255) // 256 * 256
+        return r(units * s * hg * 512 * 2) + r(units * s * hg * 2 * 4)
+    checked = 0
+    for heads in (16, 64):
+        for batch in (1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 17, 24, 31, 32, 40, 48, 63, 64, 65, 100, 128,
+                      129, 200, 256, 1000):
+            for topk in (1, 63, 64, 65, 128, 129, 500, 1000, 1024, 1025, 2047, 2048):
+                assert smla.decode_workspace_bytes(batch, heads, topk) == \
+                    expect(batch, heads, topk), (batch, heads, topk)
+                assert smla.decode_workspace_bytes_fp8(batch, heads, topk) == \
+                    expect(batch, heads, topk, fp8=True), (batch, heads, topk)
+                for tokens in (2, 4, 16):
+                    if batch * tokens <= 65535:
+                        assert smla.decode_workspace_bytes_mtp(batch, tokens, heads, topk) == \
+                            expect(batch, heads, topk, tokens=tokens), (batch, tokens, heads, topk)
+                checked += 1
+    assert checked == 2 * 25 * 12
+
+
 def test_workspace_sizes_fp8():
     import sparse_mla_decode_amd as smla
     assert smla.decode_workspace_bytes_fp8(0, 64, 2048) == 0

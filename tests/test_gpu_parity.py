@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads as wl
-from cases import (HEAD_TOL, LSE_TOL, OUT_TOL, check_parity, gpu_cache, gpu_decode, lse_err, note,
+from cases import (HEAD_TOL, decode_plan, LSE_TOL, OUT_TOL, check_parity, gpu_cache, gpu_decode, lse_err, note,
                    oracle_cache, oracle_decode, rel_l2, small_case, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -289,29 +289,8 @@ def _max_moves(scores, splits, slack=8.0):
 
 
 def _plan(batch, heads, topk, fp8=False, tokens=1):
-    """Workgroups sharing a list, and the split count, of the library's plan.
-    Splits: as many as keep the busiest XCD (32 CUs; sequence s runs on XCD
-    s % 8) at one workgroup per CU, at most 16, at most one per 64-row tile,
-    and of at most 2048 (FP8: 1024) entries.  Head groups: 32 heads (16 at 16
-    heads), or 16 at 64 heads where 32-head groups would leave splits of at
-    most two tiles and 16-head groups give as many workgroups with more."""
-    cap = 1024 if fp8 else 2048
-
-    def splits(hg):
-        s = max(1, 32 // (-(-batch // 8) * tokens * (heads // hg)))
-        s = min(s, -(-topk // 64), 16)
-        return max(s, -(-topk // cap))
-
-    def tiles(s):
-        return -(-(-(-topk // s)) // 64)
-
-    hg = 32 if heads >= 32 else 16
-    s = splits(hg)
-    if heads == 64:
-        s16 = splits(16)
-        if tiles(s) <= 2 and tiles(s16) > tiles(s) and 4 * s16 >= 2 * s:
-            hg, s = 16, s16
-    return batch * tokens * (heads // hg), s
+    """(workgroups sharing a list, splits) of the library's plan."""
+    return decode_plan(batch, heads, topk, fp8, tokens)[:2]
 
 
 def _shared_pages_case(batch, heads, pages, topk, seed):
