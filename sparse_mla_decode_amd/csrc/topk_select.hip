@@ -10,7 +10,8 @@
 // Radix select over an order-preserving 32-bit key of each fp32 score, in
 // three digits (bits 31..21, 20..10, 9..0).  Two passes read every score:
 //   pass 0: histogram of digit 0 over the query's L scores (workgroups of
-//           2048 to 16384 scores by row length: LDS histogram, then the
+//           2048 to 16384 scores by row length, all of query b on XCD
+//           b % 8, where pass 1 finds them in L2: LDS histogram, then the
 //           non-empty bins added to the query's histogram with global
 //           atomics);
 //   pass 1: every workgroup finds, from that histogram, the bin b0 holding
@@ -139,10 +140,12 @@ __device__ void find_bin(const uint32_t *hist, uint32_t k, uint32_t *scan_lds, u
 template <int kThreads, int kPer>
 __global__ __launch_bounds__(kThreads) void topk_hist_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ seq_lens,
-    int32_t topk, int32_t chunks, uint32_t *__restrict__ ws, int64_t ws_stride) {
+    int32_t topk, int32_t chunks, uint32_t *__restrict__ ws, int64_t ws_stride, int32_t batch) {
     __shared__ uint32_t h[kBins0];
-    const int64_t b = blockIdx.x / chunks;
-    const int c = (int)(blockIdx.x % chunks);
+    // workgroup i runs on XCD i % 8: query b's chunks all go to XCD b % 8
+    const int64_t b = (int64_t)((blockIdx.x >> 3) / chunks) * 8 + (blockIdx.x & 7);
+    const int c = (int)((blockIdx.x >> 3) % chunks);
+    if (b >= batch) return;
     const int tid = threadIdx.x;
     const int64_t L = min((int64_t)max(seq_lens[b], 0), ld);
     if (L <= topk) return;  // every position is selected: the finish alone
@@ -181,12 +184,14 @@ template <int kThreads, int kPer>
 __global__ __launch_bounds__(kThreads) void topk_split_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ seq_lens,
     int32_t topk, int32_t chunks, uint32_t *__restrict__ ws, int64_t ws_stride, int64_t cap,
-    int32_t *__restrict__ out) {
+    int32_t *__restrict__ out, int32_t batch) {
     __shared__ uint32_t scan_a[kThreads / 64], scan_b[kThreads / 64];  // a wave total each
     __shared__ uint32_t res_lds[2];
     __shared__ uint32_t base_lds[2];
-    const int64_t b = blockIdx.x / chunks;
-    const int c = (int)(blockIdx.x % chunks);
+    // workgroup i runs on XCD i % 8: query b's chunks all go to XCD b % 8
+    const int64_t b = (int64_t)((blockIdx.x >> 3) / chunks) * 8 + (blockIdx.x & 7);
+    const int c = (int)((blockIdx.x >> 3) % chunks);
+    if (b >= batch) return;
     const int tid = threadIdx.x;
     const int64_t L = min((int64_t)max(seq_lens[b], 0), ld);
     if (L <= topk) return;
@@ -452,11 +457,11 @@ hipError_t launch_topk_select(const float *scores, int64_t ld, const int32_t *se
     do {                                                                                       \
         const int64_t ch = 4 * (PER) * (NT);                                                   \
         const int32_t chunks = (int32_t)((ld + ch - 1) / ch);                                  \
-        const dim3 grid((unsigned)((int64_t)batch * chunks)), block(NT);                       \
+        const dim3 grid((unsigned)((int64_t)(batch + 7) / 8 * 8 * chunks)), block(NT);         \
         hipLaunchKernelGGL((topk_hist_kernel<NT, PER>), grid, block, 0, stream, scores, ld,    \
-                           seq_lens, topk, chunks, ws, stride);                                \
+                           seq_lens, topk, chunks, ws, stride, batch);                         \
         hipLaunchKernelGGL((topk_split_kernel<NT, PER>), grid, block, 0, stream, scores, ld,   \
-                           seq_lens, topk, chunks, ws, stride, cap, out);                      \
+                           seq_lens, topk, chunks, ws, stride, cap, out, batch);               \
     } while (0)
     if (ld >= kBigRow) SMLA_PASSES(512, 8);
     else if (ld >= kMidRow) SMLA_PASSES(256, 4);
