@@ -837,11 +837,11 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     // max in log2 units, sum).  Where other workgroups on this XCD read the
     // same rows again (two head groups, or several query tokens) the partials
     // are streamed past the L2 (non-temporal stores), which leaves the L2 to
-    // those rows.  Otherwise (16 heads, one token) no row is read twice, and
-    // ordinary stores leave the partials in the L2 for the merge, which runs
-    // on the same XCD.
+    // those rows.  Otherwise (one head group, one token) no row is read
+    // twice, and ordinary stores leave the partials in the L2 for the merge,
+    // which runs on the same XCD.
     const size_t pidx = (size_t)unit * splits + split;
-    const bool keep_in_l2 = MB == 1 && tokens == 1;
+    const bool keep_in_l2 = groups == 1 && tokens == 1;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int h = 8 * (i >> 2) + 4 * g2 + (i & 3);
