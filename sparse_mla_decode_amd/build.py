@@ -9,8 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsmla.so")
-SOURCES = ["smla_api.hip", "kv_quant_append.hip", "sparse_mla_decode.hip", "decode_wave.hip",
-           "stage_rows.hip", "topk_select.hip"]
+SOURCES = ["smla_api.hip", "kv_quant_append.hip", "sparse_mla_decode.hip", "stage_rows.hip",
+           "topk_select.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -64,13 +64,4 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
                                     float scale, float *out, float *lse, void *workspace,
                                     const DecodePlan &plan, RowFormat fmt, hipStream_t stream);
 
-// NVFP4 rows, 32-head groups: the wave-per-SIMD decode kernel (partials in
-// the layout the merge kernel reads when plan.splits > 1)
-hipError_t launch_decode_wave(const uint16_t *q, const uint8_t *cache, int64_t num_pages,
-                              const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens,
-                              const int32_t *topk_idx, int32_t batch, int32_t tokens, int32_t heads,
-                              int32_t topk, float scale_log2, float *out, float *lse,
-                              _Float16 *part_o, float *part_ml, const DecodePlan &plan,
-                              hipStream_t stream);
-
 }  // namespace smla

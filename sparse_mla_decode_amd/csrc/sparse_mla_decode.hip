@@ -1036,20 +1036,15 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
                        q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,      \
                        topk, scale_log2, out, lse, part_o, part_ml, batch, tokens, plan.groups,    \
                        plan.splits, plan.per_split)
-    hipError_t e;
     if (fmt == kFmtFp8) {
         if (plan.heads_per_group == 32) SMLA_LAUNCH(2, kFmtFp8);
         else SMLA_LAUNCH(1, kFmtFp8);
-        e = hipGetLastError();
-    } else if (plan.heads_per_group == 32) {
-        e = launch_decode_wave(q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, batch,
-                               tokens, heads, topk, scale_log2, out, lse, part_o, part_ml, plan,
-                               stream);
     } else {
-        SMLA_LAUNCH(1, kFmtNvfp4);
-        e = hipGetLastError();
+        if (plan.heads_per_group == 32) SMLA_LAUNCH(2, kFmtNvfp4);
+        else SMLA_LAUNCH(1, kFmtNvfp4);
     }
 #undef SMLA_LAUNCH
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
     return launch_merge(part_o, part_ml, out, lse, heads, plan, batch, tokens, stream);
 }
