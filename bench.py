@@ -52,8 +52,8 @@ def log(msg):
 # the sources each kernel family is compiled from (its .hip file and the
 # device headers it includes)
 KERNEL_SOURCES = {
-    "decode": ("sparse_mla_decode.hip", "decode_device.h"),
-    "append": ("kv_quant_append.hip",),
+    "decode": ("sparse_mla_decode.hip", "decode_device.h", "nvfp4_quant.h", "e4m3.h"),
+    "append": ("kv_quant_append.hip", "nvfp4_quant.h", "e4m3.h"),
     "select": ("topk_select.hip", "decode_device.h"),
     "staged": ("stage_rows.hip",),
 }
@@ -151,7 +151,11 @@ def summarize_counters(fetch_dir, write_dir, workload):
                 continue
             per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         calib = [v for k, vs in per.items() if "neg" in k for v in vs]
-        dec = [v for k, vs in per.items() if "sparse_mla_decode_kernel" in k for v in vs]
+        # the plain decode call only: a fused append-and-decode dispatch
+        # (template flag true: demangled "true>", mangled "Lb1E") also
+        # quantises and stores the step's new rows
+        dec = [v for k, vs in per.items() if "sparse_mla_decode_kernel" in k
+               and "true>" not in k and "Lb1E" not in k for v in vs]
         mrg = [v for k, vs in per.items() if "merge_splits_kernel" in k for v in vs]
         if not calib or not dec:
             raise SystemExit("missing calibration or decode dispatches in %s" % d)
@@ -628,6 +632,9 @@ def main():
     ap.add_argument("--path", choices=("fused", "staged"), default="fused",
                     help="decode path: the fused kernel, or the staged ablation (NVFP4 only)")
     ap.add_argument("--sets", type=int, default=0, help="rotating (q, top-k) sets (0 = auto)")
+    ap.add_argument("--step", choices=("auto", "fused", "two-calls"), default="auto",
+                    help="a one-row-per-sequence NVFP4 step as one append_decode call (fused; the "
+                         "default where it applies) or as kv_quant_append then the decode")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -738,9 +745,23 @@ def main():
         s = i % sets
         decode_fn(qs[s], cache, pt, sl, tks[s], w.softmax_scale, out=out, lse=lse, workspace=ws)
 
-    def step(i):
+    def step_two_calls(i):
         append_fn(step_rows, step_slots, cache)
         decode_call(i)
+
+    # a step that appends one row per sequence (the newest token of each) can
+    # be one fused call: the same cache bytes, out and lse as the two calls
+    fusable = (fmt == "nvfp4" and args.path == "fused" and step_rows.shape[0] == w.batch)
+    if args.step == "fused" and not fusable:
+        raise SystemExit("--step fused needs NVFP4 rows, the fused path and one new row per sequence")
+    step_kind = "fused" if (fusable and args.step != "two-calls") else "two-calls"
+
+    def step_fused(i):
+        s = i % sets
+        smla.append_decode(step_rows, step_slots, qs[s], cache, pt, sl, tks[s], w.softmax_scale,
+                           out=out, lse=lse, workspace=ws)
+
+    step = step_fused if step_kind == "fused" else step_two_calls
 
     warm_clocks(step, args.warm_seconds)
     for i in range(args.warmup):
@@ -758,6 +779,11 @@ def main():
     # many back-to-back calls with the same inputs
     dec_ms = np.array([events_ms(lambda i: decode_call(args.warmup + i), args.steps)])
     app_ms = np.array([events_ms(lambda i: append_fn(step_rows, step_slots, cache), args.steps)])
+    # the other route's step time, for comparison
+    other_ms = None
+    if fusable:
+        other = step_two_calls if step_kind == "fused" else step_fused
+        other_ms = events_ms(lambda i: other(args.warmup + i), args.steps)
 
     # algorithmic work per step (mean over the sets the timed steps used)
     used = [(args.warmup + i) % sets for i in range(args.steps)]
@@ -818,6 +844,9 @@ def main():
         "decode_tflops": round(dec_tflops, 2),
         "append_us": round(float(app_ms.mean()) * 1e3, 2),
         "gpu_us_per_step": round(gpu_step_ms * 1e3, 2),
+        "step": step_kind,
+        ("gpu_us_per_step_two_calls" if step_kind == "fused" else "gpu_us_per_step_fused"):
+            (round(other_ms * 1e3, 2) if other_ms is not None else None),
         "decode_us_flushed_median": round(flush_us, 2),
         "stream_copy_GBps": round(copy_gbps, 1),
         "decode_kv_frac_of_copy": round(dec_gbps / copy_gbps, 4),

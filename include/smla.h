@@ -284,6 +284,40 @@ int smla_topk_select(const float *scores, int64_t ld, const int32_t *seq_lens, i
                      void *stream);
 
 /*
+ * ---- Append and decode in one launch [P1 section "A kernel that reads four
+ * bits directly" (the decode); section "Four bits per latent value: where
+ * 352 comes from" (the row the append writes)] ----
+ *
+ * One decode step of sequences that each gained one token: the result, in
+ * the cache and in out/lse, is exactly that of
+ *   smla_kv_quant_append(new_rows_bf16, batch, new_slots, cache, num_pages),
+ * then smla_sparse_mla_decode(q_bf16, cache, ..., softmax_scale, out, lse),
+ * in one kernel launch (plus the split merge): every decode workgroup of
+ * sequence b quantises new row b itself and reads it from LDS wherever its
+ * list translates to slot new_slots[b]; one workgroup per sequence writes
+ * the row to the cache.
+ *
+ *   new_rows_bf16  [batch][576] BF16, device, 16-B aligned: row b is
+ *                  sequence b's newest token (latent 512 + rope 64)
+ *   new_slots      [batch] int32, device: page * 64 + row of the cache slot
+ *                  it goes to; a slot outside [0, num_pages * 64) skips the
+ *                  row (as the append does)
+ *   the rest       as for smla_sparse_mla_decode (seq_lens already count
+ *                  the new token); workspace as sized by
+ *                  smla_decode_workspace_bytes(batch, heads, topk)
+ *
+ * The slots of the new rows must be distinct, and slot new_slots[b] must be
+ * read, through the page table, by no list but sequence b's (the page that
+ * receives a sequence's newest token belongs to that sequence alone).
+ * Errors: those of the two calls it stands for.  Asynchronous on `stream`.
+ */
+int smla_append_decode(const void *new_rows_bf16, const int32_t *new_slots, const void *q_bf16,
+                       uint8_t *cache, int64_t num_pages, const int32_t *page_table,
+                       int32_t max_pages, const int32_t *seq_lens, const int32_t *topk_indices,
+                       int32_t batch, int32_t heads, int32_t topk, float softmax_scale, float *out,
+                       float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * ---- Decode that allocates nothing, for callers that cannot allocate
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc) ----

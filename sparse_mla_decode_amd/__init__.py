@@ -9,6 +9,9 @@ not been built, importing this package raises.
         rows [n,576] bf16, slot_mapping [n] int32, cache [P,64,352] uint8 (in place)
     sparse_mla_decode(q, cache, page_table, seq_lens, topk, softmax_scale)
         -> (out [B,H,512] fp32, lse [B,H] fp32)
+    append_decode(new_rows [B,576] bf16, new_slots [B] int32, q, cache, ...)
+        kv_quant_append of each sequence's newest row, then the decode, in one
+        launch (the same cache bytes, out and lse)
     kv_quant_append_fp8, sparse_mla_decode_fp8
         the same over the lean FP8 row: cache [P,64,576] uint8
     stage_rows_fp8, sparse_mla_decode_staged
@@ -50,7 +53,8 @@ EXPORTS = ("smla_strerror", "smla_version", "smla_kv_quant_append",
            "smla_decode_workspace_bytes", "smla_sparse_mla_decode", "smla_kv_quant_append_fp8",
            "smla_decode_workspace_bytes_fp8", "smla_sparse_mla_decode_fp8",
            "smla_stage_rows_fp8", "smla_decode_workspace_bytes_mtp", "smla_sparse_mla_decode_mtp",
-           "smla_topk_workspace_bytes", "smla_topk_select", "smla_sparse_mla_decode_noalloc")
+           "smla_topk_workspace_bytes", "smla_topk_select", "smla_sparse_mla_decode_noalloc",
+           "smla_append_decode")
 
 
 class SmlaError(RuntimeError):
@@ -97,6 +101,9 @@ def _load() -> ctypes.CDLL:
     lib.smla_sparse_mla_decode_noalloc.argtypes = [P, P, i64, P, i32, P, P, i32, i32, i32, f32, P,
                                                    P, P]
     lib.smla_sparse_mla_decode_noalloc.restype = ctypes.c_int
+    lib.smla_append_decode.argtypes = [P, P, P, P, i64, P, i32, P, P, i32, i32, i32, f32, P, P, P,
+                                       sz, P]
+    lib.smla_append_decode.restype = ctypes.c_int
     return lib
 
 
@@ -209,7 +216,7 @@ def kv_quant_append_fp8(rows: torch.Tensor, slot_mapping: torch.Tensor, cache: t
 
 
 def _decode(q, cache, page_table, seq_lens, topk, softmax_scale, out, lse, workspace, stream,
-            row_bytes, fn, ws_fn):
+            row_bytes, fn, ws_fn, prefix=()):
     _req(cache, "cache", torch.uint8, 3)
     dev = cache.device
     _req(q, "q", torch.bfloat16, 3, dev)
@@ -236,7 +243,7 @@ def _decode(q, cache, page_table, seq_lens, topk, softmax_scale, out, lse, works
     if workspace is None and need > 0:
         workspace = workspace_for(dev, need, stream)
     ws_ptr, ws_bytes = _req_workspace(workspace, dev)
-    _check(fn(q.data_ptr(), cache.data_ptr(), cache.shape[0], page_table.data_ptr(),
+    _check(fn(*prefix, q.data_ptr(), cache.data_ptr(), cache.shape[0], page_table.data_ptr(),
               page_table.shape[1], seq_lens.data_ptr(), topk.data_ptr(), B, H, K,
               float(softmax_scale), out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes,
               _stream_ptr(dev, stream)))
@@ -250,6 +257,25 @@ def sparse_mla_decode(q: torch.Tensor, cache: torch.Tensor, page_table: torch.Te
     """Sparse MLA decode over cache [P,64,352]; returns (out [B,H,512] fp32, lse [B,H] fp32)."""
     return _decode(q, cache, page_table, seq_lens, topk, softmax_scale, out, lse, workspace,
                    stream, ROW_BYTES, lib.smla_sparse_mla_decode, lib.smla_decode_workspace_bytes)
+
+
+def append_decode(new_rows: torch.Tensor, new_slots: torch.Tensor, q: torch.Tensor,
+                  cache: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                  topk: torch.Tensor, softmax_scale: float, out: torch.Tensor | None = None,
+                  lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  stream=None):
+    """kv_quant_append(new_rows [B,576] bf16, new_slots [B] int32, cache), then
+    sparse_mla_decode(q, cache, ...), in one launch: returns (out, lse).  The
+    slots must be distinct and each read by its own sequence's list alone."""
+    _req(cache, "cache", torch.uint8, 3)
+    dev = cache.device
+    _req(new_rows, "new_rows", torch.bfloat16, 2, dev)
+    _req(new_slots, "new_slots", torch.int32, 1, dev)
+    if tuple(new_rows.shape) != (q.shape[0], DIM) or new_slots.shape[0] != q.shape[0]:
+        raise ValueError("new_rows must be [B,576] and new_slots [B]")
+    return _decode(q, cache, page_table, seq_lens, topk, softmax_scale, out, lse, workspace,
+                   stream, ROW_BYTES, lib.smla_append_decode, lib.smla_decode_workspace_bytes,
+                   prefix=(new_rows.data_ptr(), new_slots.data_ptr()))
 
 
 def sparse_mla_decode_noalloc(q: torch.Tensor, cache: torch.Tensor, page_table: torch.Tensor,

@@ -106,7 +106,8 @@ int decode(const void *q_bf16, const uint8_t *cache, int64_t num_pages, const in
            int32_t max_pages, const int32_t *seq_lens, const int32_t *topk_indices, int32_t batch,
            int32_t tokens, int32_t heads, int32_t topk, float softmax_scale, float *out,
            float *lse, void *workspace, size_t workspace_bytes, void *stream,
-           smla::RowFormat fmt) {
+           smla::RowFormat fmt, const void *new_rows_bf16 = nullptr,
+           const int32_t *new_slots = nullptr) {
     const int bad = check_decode_args(q_bf16, cache, num_pages, page_table, max_pages, seq_lens,
                                       topk_indices, batch, tokens, heads, topk, out, lse);
     if (bad != SMLA_OK) return bad;
@@ -120,7 +121,7 @@ int decode(const void *q_bf16, const uint8_t *cache, int64_t num_pages, const in
     const hipError_t e = smla::launch_sparse_mla_decode(
         static_cast<const uint16_t *>(q_bf16), cache, num_pages, page_table, max_pages, seq_lens,
         topk_indices, batch, tokens, heads, topk, softmax_scale, out, lse, workspace, plan, fmt,
-        static_cast<hipStream_t>(stream));
+        static_cast<hipStream_t>(stream), static_cast<const uint16_t *>(new_rows_bf16), new_slots);
     return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
@@ -146,6 +147,18 @@ int smla_sparse_mla_decode(const void *q_bf16, const uint8_t *cache, int64_t num
     return decode(q_bf16, cache, num_pages, page_table, max_pages, seq_lens, topk_indices, batch,
                   1, heads, topk, softmax_scale, out, lse, workspace, workspace_bytes, stream,
                   smla::kFmtNvfp4);
+}
+
+int smla_append_decode(const void *new_rows_bf16, const int32_t *new_slots, const void *q_bf16,
+                       uint8_t *cache, int64_t num_pages, const int32_t *page_table,
+                       int32_t max_pages, const int32_t *seq_lens, const int32_t *topk_indices,
+                       int32_t batch, int32_t heads, int32_t topk, float softmax_scale, float *out,
+                       float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!new_rows_bf16 || !new_slots) return SMLA_ERR_NULL;
+    if (!aligned(new_rows_bf16, 16) || !aligned(new_slots, 4)) return SMLA_ERR_ALIGN;
+    return decode(q_bf16, cache, num_pages, page_table, max_pages, seq_lens, topk_indices, batch,
+                  1, heads, topk, softmax_scale, out, lse, workspace, workspace_bytes, stream,
+                  smla::kFmtNvfp4, new_rows_bf16, new_slots);
 }
 
 int smla_kv_quant_append_fp8(const void *rows_bf16, int64_t n, const int32_t *slot_mapping,

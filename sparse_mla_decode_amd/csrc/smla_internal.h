@@ -62,6 +62,8 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
                                     const int32_t *seq_lens, const int32_t *topk_idx,
                                     int32_t batch, int32_t tokens, int32_t heads, int32_t topk,
                                     float scale, float *out, float *lse, void *workspace,
-                                    const DecodePlan &plan, RowFormat fmt, hipStream_t stream);
+                                    const DecodePlan &plan, RowFormat fmt, hipStream_t stream,
+                                    const uint16_t *new_rows = nullptr,
+                                    const int32_t *new_slots = nullptr);
 
 }  // namespace smla

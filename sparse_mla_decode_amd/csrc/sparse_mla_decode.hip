@@ -47,6 +47,7 @@
 //     workgroup, an L2 writeback, which costs more than the launch).
 #include "smla_internal.h"
 #include "decode_device.h"
+#include "nvfp4_quant.h"
 
 #include <type_traits>
 
@@ -91,16 +92,27 @@ template <> struct Ring<kFmtFp8> {
 // banks instead of the two that a 576-byte row stride leaves them.
 __device__ __forceinline__ int fp8_swz(int r) { return ((r >> 1) & 3) << 1; }
 
-template <int MB, int FMT>
+// FUSED (NVFP4 rows, one query token): the call appends each sequence's
+// newest BF16 row first (new_rows [batch][576], new_slots [batch]), with the
+// result of kv_quant_append followed by the decode.  Every workgroup of
+// sequence sq quantises that row itself into LDS (the append's own code) and
+// puts those bytes into its tiles wherever a list entry translates to slot
+// new_slots[sq] (the bytes its loads fetched from the cache there may
+// predate the append); the workgroup of split 0 and head group 0 writes the
+// row to the cache.  The slot must be read by no other sequence's list in
+// the same call.
+template <int MB, int FMT, bool FUSED = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ cache,
+void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, uint8_t *__restrict__ cache,
                               int64_t num_pages, const int32_t *__restrict__ page_table,
                               int32_t max_pages, const int32_t *__restrict__ seq_lens,
                               const int32_t *__restrict__ topk_idx, int32_t heads, int32_t topk,
                               float scale_log2, float *__restrict__ out, float *__restrict__ lse,
                               _Float16 *__restrict__ part_o, float *__restrict__ part_ml,
                               int32_t batch, int32_t tokens, int32_t groups, int32_t splits,
-                              int32_t per_split) {
+                              int32_t per_split, const uint16_t *__restrict__ new_rows,
+                              const int32_t *__restrict__ new_slots) {
+    static_assert(!FUSED || FMT == kFmtNvfp4, "the fused append writes NVFP4 rows");
     constexpr int HG = 16 * MB;  // heads of this workgroup
     using R = Ring<FMT>;
     constexpr bool kFp8 = FMT == kFmtFp8;
@@ -125,6 +137,10 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
     __shared__ float m_lds[32];
     __shared__ int32_t scan_lds[8];
     __shared__ __attribute__((aligned(16))) uint32_t flag_lds[2][4];
+    // FUSED: the new row's 352 bytes, and which compacted list entries of
+    // the split read its slot (bit p of word p / 32)
+    __shared__ __attribute__((aligned(16))) uint8_t fresh_lds[FUSED ? kRowBytes : 16];
+    __shared__ __attribute__((aligned(8))) uint32_t fresh_mask[FUSED ? R::kMaxPerSplit / 32 : 2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -221,6 +237,33 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
             wait_vmcnt(after * n_dma);
         }
     };
+    // FUSED: the new row's slot (none: all ones); score wave 0 quantises the
+    // row into fresh_lds before anything else (the append's own code) and,
+    // in the workgroup of split 0 and head group 0, writes it to the cache;
+    // the value waves clear the entry mask
+    uint32_t fresh_slot = 0xFFFFFFFFu;
+    if constexpr (FUSED) {
+        const int64_t ns = new_slots[sq];
+        if (ns >= 0 && ns < num_pages * kPageRows) fresh_slot = (uint32_t)ns;
+        if (wave == 0 && lane < 32) {
+            // lane j: latent block j and rope values 2j, 2j+1
+            const uint16_t *x = new_rows + (int64_t)sq * kDim;
+            const uint4 lo = *reinterpret_cast<const uint4 *>(x + lane * kBlock);
+            const uint4 hi = *reinterpret_cast<const uint4 *>(x + lane * kBlock + 8);
+            const uint32_t r = *reinterpret_cast<const uint32_t *>(x + kLatent + 2 * lane);
+            const Nvfp4Lane v = nvfp4_quant_lane(lo, hi, r);
+            *reinterpret_cast<uint2 *>(fresh_lds + lane * 8) = make_uint2(v.nib[0], v.nib[1]);
+            fresh_lds[kScaleOff + lane] = (uint8_t)v.scale;
+            *reinterpret_cast<uint16_t *>(fresh_lds + kRopeOff + 2 * lane) = (uint16_t)v.rope;
+            if (split == 0 && hg == 0 && fresh_slot != 0xFFFFFFFFu) {
+                uint8_t *dst = cache + (size_t)fresh_slot * kRowBytes;
+                *reinterpret_cast<uint2 *>(dst + lane * 8) = make_uint2(v.nib[0], v.nib[1]);
+                dst[kScaleOff + lane] = (uint8_t)v.scale;
+                *reinterpret_cast<uint16_t *>(dst + kRopeOff + 2 * lane) = (uint16_t)v.rope;
+            }
+        }
+        if (tid >= 256 && tid - 256 < R::kMaxPerSplit / 32) fresh_mask[tid - 256] = 0u;
+    }
     if (wave < 4) {
         // =========================== score waves ===========================
         if (MB == 1) {  // rows 16..31 of both weight tiles stay zero: MFMA 32x32 over 16 heads
@@ -386,8 +429,31 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
                         (_Float16)__builtin_amdgcn_exp2f(d[mb][r]);
         };
 
+        // FUSED: the rows of this wave (16 sw ..) in tile T that read the new
+        // slot get the new row's bytes in LDS before the wave reads them
+        // (the tile's loads have landed: it is complete one barrier before);
+        // the value waves read them two barriers later
+        auto patch_rows = [&](int T) {
+            if constexpr (FUSED) {
+                if (fresh_slot == 0xFFFFFFFFu) return;
+                const uint32_t m16 = (__builtin_amdgcn_readfirstlane(fresh_mask[2 * T + (sw >> 1)]) >>
+                                      (16 * (sw & 1))) & 0xFFFFu;
+                if (m16 == 0) return;
+                for (int i = 0; i < 16; ++i) {
+                    if (!((m16 >> i) & 1u)) continue;
+                    const int r = 16 * sw + i;
+                    if (lane < kRowBytes / 16)
+                        *reinterpret_cast<uint4 *>(ring + (T % kNBuf) * kTileBytes + r * kRowB +
+                                                   16 * (lane ^ nv_swz(r))) =
+                            *reinterpret_cast<const uint4 *>(fresh_lds + 16 * lane);
+                }
+            }
+        };
         Packed pk;
-        if (n_tiles > 0) load_packed(0, pk);
+        if (n_tiles > 0) {
+            patch_rows(0);
+            load_packed(0, pk);
+        }
         float dp[MB][4];  // d of the previous tile, for a re-weight
 
         for (int s = 0; s <= n_tiles + 1; ++s) {
@@ -462,7 +528,10 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
             if (s >= n_tiles) continue;
             // (c) this wave's packed bytes of tile s + 1 (complete since
             // B(s)), issued first so that the reads complete under (d)
-            if (s + 1 < n_tiles) load_packed(s + 1, pk);
+            if (s + 1 < n_tiles) {
+                patch_rows(s + 1);
+                load_packed(s + 1, pk);
+            }
             // (d) weights of tile s, the tile's transposed block scales for
             // the value waves, and the flag (any score past max + kSlack)
             const int pb = s & 1;
@@ -585,7 +654,10 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, const uint8_t *__r
         for (int w = 0; w < 3; ++w) pos += (w < wave - 4) ? scan_lds[w] : 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            if (rid[i] != 0xFFFFFFFFu) rowid_lds[pos++] = rid[i];
+            if (rid[i] != 0xFFFFFFFFu) {
+                if (FUSED && rid[i] == fresh_slot) atomicOr(&fresh_mask[pos >> 5], 1u << (pos & 31));
+                rowid_lds[pos++] = rid[i];
+            }
         if (tid - 256 < n_pad - n_valid) rowid_lds[n_valid + tid - 256] = 0u;
     }
     __syncthreads();
@@ -1018,8 +1090,11 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
                                     const int32_t *seq_lens, const int32_t *topk_idx,
                                     int32_t batch, int32_t tokens, int32_t heads, int32_t topk,
                                     float scale, float *out, float *lse, void *workspace,
-                                    const DecodePlan &plan, RowFormat fmt, hipStream_t stream) {
+                                    const DecodePlan &plan, RowFormat fmt, hipStream_t stream,
+                                    const uint16_t *new_rows, const int32_t *new_slots) {
     const int blocks = ((batch + 7) / 8) * 8 * tokens * plan.groups * plan.splits;
+    const bool fused = new_rows != nullptr;
+    if (fused && (fmt != kFmtNvfp4 || tokens != 1)) return hipErrorInvalidValue;
     const int units = batch * tokens * plan.groups;
     _Float16 *part_o = nullptr;
     float *part_ml = nullptr;
@@ -1031,17 +1106,22 @@ hipError_t launch_sparse_mla_decode(const uint16_t *q, const uint8_t *cache, int
                                             ((o_bytes + 255) & ~(size_t)255));
     }
     const float scale_log2 = (float)((double)scale * 1.4426950408889634074);
-#define SMLA_LAUNCH(MB, FMT)                                                                 \
-    hipLaunchKernelGGL((sparse_mla_decode_kernel<MB, FMT>), dim3(blocks), dim3(kThreads), 0, stream, \
-                       q, cache, num_pages, page_table, max_pages, seq_lens, topk_idx, heads,      \
-                       topk, scale_log2, out, lse, part_o, part_ml, batch, tokens, plan.groups,    \
-                       plan.splits, plan.per_split)
+    // the kernel writes the cache only when it appends (FUSED)
+    uint8_t *cache_rw = const_cast<uint8_t *>(cache);
+#define SMLA_LAUNCH(MB, FMT, FU)                                                               \
+    hipLaunchKernelGGL((sparse_mla_decode_kernel<MB, FMT, FU>), dim3(blocks), dim3(kThreads), 0, \
+                       stream, q, cache_rw, num_pages, page_table, max_pages, seq_lens, topk_idx,    \
+                       heads, topk, scale_log2, out, lse, part_o, part_ml, batch, tokens,            \
+                       plan.groups, plan.splits, plan.per_split, new_rows, new_slots)
     if (fmt == kFmtFp8) {
-        if (plan.heads_per_group == 32) SMLA_LAUNCH(2, kFmtFp8);
-        else SMLA_LAUNCH(1, kFmtFp8);
+        if (plan.heads_per_group == 32) SMLA_LAUNCH(2, kFmtFp8, false);
+        else SMLA_LAUNCH(1, kFmtFp8, false);
+    } else if (fused) {
+        if (plan.heads_per_group == 32) SMLA_LAUNCH(2, kFmtNvfp4, true);
+        else SMLA_LAUNCH(1, kFmtNvfp4, true);
     } else {
-        if (plan.heads_per_group == 32) SMLA_LAUNCH(2, kFmtNvfp4);
-        else SMLA_LAUNCH(1, kFmtNvfp4);
+        if (plan.heads_per_group == 32) SMLA_LAUNCH(2, kFmtNvfp4, false);
+        else SMLA_LAUNCH(1, kFmtNvfp4, false);
     }
 #undef SMLA_LAUNCH
     hipError_t e = hipGetLastError();
