@@ -1,6 +1,7 @@
-// Quantisation of one BF16 KV row into the 352-byte NVFP4 row, by 32 lanes:
-// lane j takes latent block j (values 16j .. 16j+15) and rope values 2j,
-// 2j+1.  Format: "Prime Inference: serving GLM-5.3 to agents is a KV-cache
+// Quantisation of one BF16 KV row into the 352-byte NVFP4 row, by 32 lanes
+// (lane j takes latent block j, values 16j .. 16j+15, and rope values 2j,
+// 2j+1) or by four waves of 64 lanes (two latent values per lane).
+// Format: "Prime Inference: serving GLM-5.3 to agents is a KV-cache
 // problem", section "Four bits per latent value: where 352 comes from" (512
 // e2m1 values with one E4M3 scale per 16, the 64 rope values as E4M3).  The
 // rounding rules (scale = E4M3 nearest amax/6, nibble = e2m1 nearest x/scale,
@@ -49,6 +50,12 @@ __device__ __forceinline__ uint32_t nvfp4_e2m1_code(float a, const float t[7]) {
     return c;
 }
 
+// E4M3 codes of a BF16 pair (low half first) as two bytes, the rope rule.
+__device__ __forceinline__ uint32_t nvfp4_rope_pair(uint32_t r) {
+    return e4m3_nearest(__uint_as_float((r & 0xFFFFu) << 16)) |
+           (e4m3_nearest(__uint_as_float(r & 0xFFFF0000u)) << 8);
+}
+
 // One lane's share of the row: its block's 16 nibbles (value 16j + i in
 // bits 4 (i % 8) of word i / 8), its block scale, its two rope bytes.
 struct Nvfp4Lane {
@@ -81,10 +88,35 @@ __device__ __forceinline__ Nvfp4Lane nvfp4_quant_lane(uint4 lo, uint4 hi, uint32
         o.nib[i >> 3] |= nib << ((i & 7) * 4);
     }
     o.scale = s;
-    const uint32_t c0 = e4m3_nearest(__uint_as_float((r & 0xFFFFu) << 16));
-    const uint32_t c1 = e4m3_nearest(__uint_as_float(r & 0xFFFF0000u));
-    o.rope = c0 | (c1 << 8);
+    o.rope = nvfp4_rope_pair(r);
     return o;
+}
+
+// The same encoding with 64 lanes per 128 latent values: lane l takes
+// values 2 (l % 8) and 2 (l % 8) + 1 of block l / 8 (w: that BF16 pair, low
+// half first).  The block's amax is the largest magnitude over its 8 lanes
+// (DPP quad swaps, then the half-row mirror; integer maxima of the BF16
+// magnitude bits, as above), so every decision is the one nvfp4_quant_lane
+// takes.  Returns the byte of the two nibbles (value 2 (l % 8) low); *scale
+// receives the block's scale code.
+__device__ __forceinline__ uint32_t nvfp4_quant_pair(uint32_t w, uint32_t *scale) {
+    uint32_t a = max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
+    a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+    a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+    a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x141, 0xF, 0xF, true));  // row_half_mirror
+    const float amax = __uint_as_float(a << 16);
+    const uint32_t s = nvfp4_scale_code(amax);
+    const float S = e4m3_mag(s);
+    const float t[7] = {0.25f * S, 0.75f * S, 1.25f * S, 1.75f * S, 2.5f * S, 3.5f * S, 5.0f * S};
+    uint32_t byte = 0u;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t h = i ? (w >> 16) : (w & 0xFFFFu);
+        const uint32_t mag = (S == 0.0f) ? 0u : nvfp4_e2m1_code(__uint_as_float((h & 0x7FFFu) << 16), t);
+        byte |= (mag | ((h >> 12) & 8u)) << (4 * i);
+    }
+    *scale = s;
+    return byte;
 }
 
 }  // namespace smla

@@ -140,7 +140,15 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, uint8_t *__restric
     // FUSED: the new row's 352 bytes, and which compacted list entries of
     // the split read its slot (bit p of word p / 32)
     __shared__ __attribute__((aligned(16))) uint8_t fresh_lds[FUSED ? kRowBytes : 16];
+    // FUSED: the new BF16 row as the score waves load it (score wave w: 1 KB
+    // holding latent values 128 w .. 128 w + 127, then rope values 16 w ..
+    // 16 w + 15, then repeats of the last 16 bytes)
+    __shared__ __attribute__((aligned(16))) uint8_t fresh_raw[FUSED ? 4 * 1024 : 16];
     __shared__ __attribute__((aligned(8))) uint32_t fresh_mask[FUSED ? R::kMaxPerSplit / 32 : 2];
+    // FUSED: bit T of fresh_tiles[w] is set when rows 16 w .. 16 w + 15 of
+    // tile T hold a marked entry (a split has at most 32 tiles)
+    __shared__ uint32_t fresh_tiles[4];
+    static_assert(!FUSED || R::kMaxPerSplit <= 32 * kTile, "one bit per tile");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -237,32 +245,16 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, uint8_t *__restric
             wait_vmcnt(after * n_dma);
         }
     };
-    // FUSED: the new row's slot (none: all ones); score wave 0 quantises the
-    // row into fresh_lds before anything else (the append's own code) and,
-    // in the workgroup of split 0 and head group 0, writes it to the cache;
-    // the value waves clear the entry mask
+    // FUSED: the new row's slot (none: all ones); the score waves quantise
+    // the row (below); the value waves clear the entry mask and the tile
+    // summary
     uint32_t fresh_slot = 0xFFFFFFFFu;
     if constexpr (FUSED) {
         const int64_t ns = new_slots[sq];
         if (ns >= 0 && ns < num_pages * kPageRows) fresh_slot = (uint32_t)ns;
-        if (wave == 0 && lane < 32) {
-            // lane j: latent block j and rope values 2j, 2j+1
-            const uint16_t *x = new_rows + (int64_t)sq * kDim;
-            const uint4 lo = *reinterpret_cast<const uint4 *>(x + lane * kBlock);
-            const uint4 hi = *reinterpret_cast<const uint4 *>(x + lane * kBlock + 8);
-            const uint32_t r = *reinterpret_cast<const uint32_t *>(x + kLatent + 2 * lane);
-            const Nvfp4Lane v = nvfp4_quant_lane(lo, hi, r);
-            *reinterpret_cast<uint2 *>(fresh_lds + lane * 8) = make_uint2(v.nib[0], v.nib[1]);
-            fresh_lds[kScaleOff + lane] = (uint8_t)v.scale;
-            *reinterpret_cast<uint16_t *>(fresh_lds + kRopeOff + 2 * lane) = (uint16_t)v.rope;
-            if (split == 0 && hg == 0 && fresh_slot != 0xFFFFFFFFu) {
-                uint8_t *dst = cache + (size_t)fresh_slot * kRowBytes;
-                *reinterpret_cast<uint2 *>(dst + lane * 8) = make_uint2(v.nib[0], v.nib[1]);
-                dst[kScaleOff + lane] = (uint8_t)v.scale;
-                *reinterpret_cast<uint16_t *>(dst + kRopeOff + 2 * lane) = (uint16_t)v.rope;
-            }
-        }
         if (tid >= 256 && tid - 256 < R::kMaxPerSplit / 32) fresh_mask[tid - 256] = 0u;
+        if (tid >= 256 + R::kMaxPerSplit / 32 && tid - 256 - R::kMaxPerSplit / 32 < 4)
+            fresh_tiles[tid - 256 - R::kMaxPerSplit / 32] = 0u;
     }
     if (wave < 4) {
         // =========================== score waves ===========================
@@ -280,11 +272,44 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, uint8_t *__restric
         // step.  The staging area starts at ring slot 3, whose first tile is
         // loaded only after the initial barrier.
         const uint32_t q_lds = ring_addr + 3u * kTileBytes;
+        // FUSED: this wave's quarter of the new row, HBM -> LDS ahead of its
+        // query loads (lane l < 16: latent piece l, lanes 16, 17: rope pieces;
+        // the other lanes repeat piece 17 into the rest of the 1 KB)
+        if constexpr (FUSED) {
+            const int pc = lane < 18 ? lane : 17;
+            const uint16_t *x = new_rows + (int64_t)sq * kDim;
+            dma16(pc < 16 ? x + 128 * sw + 8 * pc : x + kLatent + 16 * sw + 8 * (pc - 16),
+                  (uint32_t)(size_t)(lds_void_t *)fresh_raw + (uint32_t)sw * 1024u);
+        }
         for (int i = sw; i < MB * kKSteps; i += 4) {
             const int mb = i / kKSteps, j = i % kKSteps;
             const int d0 = (j < 16) ? (128 * g + 8 * j) : (512 + 16 * g + 8 * (j - 16));
             dma16(q + ((int64_t)b * heads + hg * HG + mb * 16 + n) * kDim + d0,
                   q_lds + (uint32_t)i * 1024u);
+        }
+        // FUSED: once the row's loads have landed (the query loads issued
+        // after them may still be in flight), its quarter is quantised with
+        // the append's code into fresh_lds and, in the workgroup of split 0
+        // and head group 0, written to the cache: lane l gives the nibble
+        // byte of latent values 128 sw + 2 l, + 1; lane 8 k also the scale of
+        // block 8 sw + k; lanes l < 8 the rope bytes 16 sw + 2 l, + 1
+        if constexpr (FUSED) {
+            wait_vmcnt((MB * kKSteps - sw + 3) / 4);
+            const uint32_t *raw = reinterpret_cast<const uint32_t *>(fresh_raw + sw * 1024);
+            uint32_t sc;
+            const uint32_t nb = nvfp4_quant_pair(raw[lane], &sc);
+            const uint32_t rp = lane < 8 ? nvfp4_rope_pair(raw[64 + lane]) : 0u;
+            const int blk = 8 * sw + (lane >> 3);
+            fresh_lds[64 * sw + lane] = (uint8_t)nb;
+            if ((lane & 7) == 0) fresh_lds[kScaleOff + blk] = (uint8_t)sc;
+            if (lane < 8)
+                *reinterpret_cast<uint16_t *>(fresh_lds + kRopeOff + 16 * sw + 2 * lane) = (uint16_t)rp;
+            if (split == 0 && hg == 0 && fresh_slot != 0xFFFFFFFFu) {
+                uint8_t *dst = cache + (size_t)fresh_slot * kRowBytes;
+                dst[64 * sw + lane] = (uint8_t)nb;
+                if ((lane & 7) == 0) dst[kScaleOff + blk] = (uint8_t)sc;
+                if (lane < 8) *reinterpret_cast<uint16_t *>(dst + kRopeOff + 16 * sw + 2 * lane) = (uint16_t)rp;
+            }
         }
         // the two barriers of the value waves' prologue; the query is in LDS
         // after the second
@@ -293,6 +318,10 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, uint8_t *__restric
         const int n_tiles = (n_valid + kTile - 1) / kTile;
         wait_vmcnt_n<0>();
         __syncthreads();
+        // FUSED: the tiles in which this wave's rows take the new row
+        // (complete after the second barrier)
+        uint32_t my_tiles = 0u;
+        if constexpr (FUSED) my_tiles = __builtin_amdgcn_readfirstlane(fresh_tiles[sw]);
         // The query in registers as f16 A operands: A[m = head][k = 8g+i] at
         // score step j holds dim 128g + 8j + i (latent, j < 16) or
         // 512 + 16g + 8(j-16) + i (rope), the dims the row unpack produces.
@@ -435,7 +464,7 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, uint8_t *__restric
         // the value waves read them two barriers later
         auto patch_rows = [&](int T) {
             if constexpr (FUSED) {
-                if (fresh_slot == 0xFFFFFFFFu) return;
+                if (!((my_tiles >> T) & 1u)) return;
                 const uint32_t m16 = (__builtin_amdgcn_readfirstlane(fresh_mask[2 * T + (sw >> 1)]) >>
                                       (16 * (sw & 1))) & 0xFFFFu;
                 if (m16 == 0) return;
@@ -655,7 +684,10 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, uint8_t *__restric
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             if (rid[i] != 0xFFFFFFFFu) {
-                if (FUSED && rid[i] == fresh_slot) atomicOr(&fresh_mask[pos >> 5], 1u << (pos & 31));
+                if (FUSED && rid[i] == fresh_slot) {
+                    atomicOr(&fresh_mask[pos >> 5], 1u << (pos & 31));
+                    atomicOr(&fresh_tiles[(pos >> 4) & 3], 1u << (pos >> 6));
+                }
                 rowid_lds[pos++] = rid[i];
             }
         if (tid - 256 < n_pad - n_valid) rowid_lds[n_valid + tid - 256] = 0u;
