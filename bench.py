@@ -175,6 +175,14 @@ def summarize_counters(fetch_dir, write_dir, workload):
     return "\n".join(lines)
 
 
+def step_fusable(args, w) -> bool:
+    """A decode step can be one append_decode call: NVFP4 rows, the fused
+    decode path, and one new row per sequence (the workloads whose step
+    appends no multi-row tail)."""
+    return (args.op == "decode" and args.format == "nvfp4" and args.path == "fused"
+            and not w.append_tail)
+
+
 def warm_clocks(fn, seconds):
     """Untimed calls fn(0), fn(1), ... until `seconds` of wall time have
     passed, then a synchronisation: the GPU's clocks rise over the first tens
@@ -664,13 +672,17 @@ def main():
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
+    import workloads as wl
+    w = wl.WORKLOADS[args.workload]
+    if args.step == "fused" and not step_fusable(args, w):
+        raise SystemExit("--step fused needs the decode op, NVFP4 rows, the fused path and a "
+                         "workload that appends one row per sequence per step")
+
     import torch
     import sparse_mla_decode_amd as smla
-    import workloads as wl
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = wl.WORKLOADS[args.workload]
     if args.op == "select":
         bench_select(args, w, dev)
         return
@@ -751,9 +763,8 @@ def main():
 
     # a step that appends one row per sequence (the newest token of each) can
     # be one fused call: the same cache bytes, out and lse as the two calls
-    fusable = (fmt == "nvfp4" and args.path == "fused" and step_rows.shape[0] == w.batch)
-    if args.step == "fused" and not fusable:
-        raise SystemExit("--step fused needs NVFP4 rows, the fused path and one new row per sequence")
+    fusable = step_fusable(args, w)
+    assert not fusable or step_rows.shape[0] == w.batch
     step_kind = "fused" if (fusable and args.step != "two-calls") else "two-calls"
 
     def step_fused(i):

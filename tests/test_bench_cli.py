@@ -25,6 +25,17 @@ def test_help_lists_the_timing_flags():
         assert flag in r.stdout
 
 
+def test_fused_step_refused_where_it_does_not_apply():
+    # refused before any GPU work: FP8 rows, the staged path, and workloads
+    # whose step appends a multi-row tail
+    for extra in (["--format", "fp8"], ["--path", "staged"], ["--workload", "ragged"],
+                  ["--workload", "million"], ["--op", "mtp"]):
+        r = run_bench("--step", "fused", *extra)
+        assert r.returncode != 0, extra
+        assert "--step fused needs" in r.stderr, extra
+        assert r.stdout.strip() == ""
+
+
 def test_traffic_record_format():
     # the stored HBM counter figures are keyed by the decode kernel's source
     # hash (bench.py reports them only for the kernel they were taken on), and

@@ -1,5 +1,5 @@
-"""The hot path under HIP graph capture: a decode step (append + decode) and a
-select + decode step are captured once and replayed several times, with the
+"""The hot path under HIP graph capture: a decode step (append + decode, and
+the same as one fused call) and a select + decode step are captured once and replayed several times, with the
 program's own eager work and synchronisations between the replays (the calls
 use no memset, allocation or host sync).  Every replay must equal the eager
 result: bit for bit for the decode over a fixed list (deterministic), as a
@@ -58,16 +58,23 @@ def test_graph_replays_equal_eager(dev, smla):
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     out2 = torch.empty_like(out)
     lse2 = torch.empty_like(lse)
+    out3 = torch.empty_like(out)
+    lse3 = torch.empty_like(lse)
     sel = torch.empty((B, w.topk), dtype=torch.int32, device=dev)
     ws = torch.zeros(max(smla.decode_workspace_bytes(B, H, w.topk), 256), dtype=torch.uint8,
                      device=dev)
     ws2 = torch.zeros_like(ws)
+    ws3 = torch.zeros_like(ws)
     tws = smla.topk_workspace(dev, B, scores.shape[1])
 
     def step(s):
         smla.kv_quant_append(rows, slots, cache, stream=s)
         smla.sparse_mla_decode(q, cache, pt, sl, tk, w.softmax_scale, out=out, lse=lse,
                                workspace=ws, stream=s)
+        # the fused call appends the same rows again (the same bytes) and
+        # decodes the same lists: out3, lse3 equal out, lse bit for bit
+        smla.append_decode(rows, slots, q, cache, pt, sl, tk, w.softmax_scale, out=out3,
+                           lse=lse3, workspace=ws3, stream=s)
         smla.topk_select(scores, sl, w.topk, out=sel, workspace=tws, stream=s)
         smla.sparse_mla_decode(q, cache, pt, sl, sel, w.softmax_scale, out=out2, lse=lse2,
                                workspace=ws2, stream=s)
@@ -76,6 +83,7 @@ def test_graph_replays_equal_eager(dev, smla):
     step(None)
     torch.cuda.synchronize(dev)
     ref = [t.clone() for t in (out, lse, out2, lse2)]
+    assert torch.equal(out3, ref[0]) and torch.equal(lse3, ref[1]), "eager fused call"
     ref_sel = torch.sort(sel, dim=1).values.clone()
 
     def rel(a, b):
@@ -93,13 +101,14 @@ def test_graph_replays_equal_eager(dev, smla):
     torch.cuda.current_stream(dev).wait_stream(s)
     torch.cuda.synchronize(dev)
     for rep in range(5):
-        for t in (out, lse, out2, lse2, sel):
+        for t in (out, lse, out2, lse2, out3, lse3, sel):
             t.fill_(-1 if t.dtype == torch.int32 else float("nan"))
         q.mul_(1.0)                                   # eager work between replays
         torch.cuda.synchronize(dev)
         g.replay()
         torch.cuda.synchronize(dev)
         assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), "replay %d decode" % rep
+        assert torch.equal(out3, ref[0]) and torch.equal(lse3, ref[1]), "replay %d fused" % rep
         assert torch.equal(torch.sort(sel, dim=1).values, ref_sel), "replay %d select" % rep
         # another order of the same list regroups rows into tiles: each f16
         # weight moves by <= 2^-11 relative
