@@ -269,6 +269,7 @@ def append_decode(new_rows: torch.Tensor, new_slots: torch.Tensor, q: torch.Tens
     slots must be distinct and each read by its own sequence's list alone."""
     _req(cache, "cache", torch.uint8, 3)
     dev = cache.device
+    _req(q, "q", torch.bfloat16, 3, dev)
     _req(new_rows, "new_rows", torch.bfloat16, 2, dev)
     _req(new_slots, "new_slots", torch.int32, 1, dev)
     if tuple(new_rows.shape) != (q.shape[0], DIM) or new_slots.shape[0] != q.shape[0]:
