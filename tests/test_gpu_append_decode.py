@@ -40,23 +40,13 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case_i", range(len(CASES)))
-def test_append_decode_matches_two_calls(dev, smla, case_i):
-    B, H, lens, K, copies = CASES[case_i]
-    note("append_decode B=%d H=%d K=%d" % (B, H, K))
-    c = small_case(B, H, lens, K, seed=40 + case_i, pad=K // 8)
-    rng = np.random.default_rng(70 + case_i)
+def fused_against_two_calls(dev, smla, c, new_slots):
+    """The newest token of every sequence appended at new_slots (-1: not
+    appended) and decoded, by the fused call and by the two calls, on copies
+    of one cache holding every older token; then both against the oracle."""
+    B = c["q"].shape[0]
     lens = c["lens"]
-    # the newest token's position in some lists (replacing entries)
-    for b in range(B):
-        if copies[b]:
-            pos = rng.choice(K, copies[b], replace=False)
-            c["topk"][b, pos] = int(lens[b]) - 1
     new_bits = np.stack([c["rows"][b][int(lens[b]) - 1] for b in range(B)])
-    new_slots = np.array([wl.slots_for(c["pt"], b, int(lens[b]) - 1, 1)[0] for b in range(B)],
-                         dtype=np.int32)
-    new_slots[-1] = -1  # the last sequence's row is not appended
-
     base = torch.zeros((c["num_pages"], 64, 352), dtype=torch.uint8, device=dev)
     for b in range(B):
         n = int(lens[b]) - 1
@@ -89,6 +79,49 @@ def test_append_decode_matches_two_calls(dev, smla, case_i):
     assert np.array_equal(cache_one.cpu().numpy(), ref_cache)
     ro, rl = oracle.sparse_mla_decode(c["q"], ref_cache, c["pt"], lens, c["topk"], c["scale"])
     check_parity(o1.cpu().numpy(), ro, l1.cpu().numpy(), rl, "append_decode")
+    return o1.cpu().numpy(), l1.cpu().numpy()
+
+
+def newest_slots(c):
+    lens = c["lens"]
+    return np.array([wl.slots_for(c["pt"], b, int(lens[b]) - 1, 1)[0] for b in range(lens.size)],
+                    dtype=np.int32)
+
+
+@pytest.mark.parametrize("case_i", range(len(CASES)))
+def test_append_decode_matches_two_calls(dev, smla, case_i):
+    B, H, lens, K, copies = CASES[case_i]
+    note("append_decode B=%d H=%d K=%d" % (B, H, K))
+    c = small_case(B, H, lens, K, seed=40 + case_i, pad=K // 8)
+    rng = np.random.default_rng(70 + case_i)
+    lens = c["lens"]
+    # the newest token's position in some lists (replacing entries)
+    for b in range(B):
+        if copies[b]:
+            pos = rng.choice(K, copies[b], replace=False)
+            c["topk"][b, pos] = int(lens[b]) - 1
+    new_slots = newest_slots(c)
+    new_slots[-1] = -1  # the last sequence's row is not appended
+    fused_against_two_calls(dev, smla, c, new_slots)
+
+
+def test_append_decode_first_tokens_and_empty_lists(dev, smla):
+    """Edge cases: a sequence whose only token is the new one (its list
+    selects that token alone), a list with no usable entry (out 0, lse -inf,
+    and the new row still reaches the cache), a new token that opens a page
+    (position 64) and is the last entry of its list, and one in the middle
+    of a 64-head list."""
+    note("append_decode edge cases")
+    K = 256
+    c = small_case(4, 64, [1, 40, 65, 700], K, seed=77)
+    c["topk"][0, :] = -1
+    c["topk"][0, 5] = 0
+    c["topk"][1, :] = -1
+    c["topk"][2, :] = -1
+    c["topk"][2, :65] = np.arange(65, dtype=np.int32)
+    c["topk"][3, K // 2] = 699
+    out, lse = fused_against_two_calls(dev, smla, c, newest_slots(c))
+    assert not out[1].any() and np.isneginf(lse[1]).all()
 
 
 def test_append_decode_full_tp4_step(dev, smla):
