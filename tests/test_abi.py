@@ -138,6 +138,34 @@ def test_decode_rejects_bad_arguments(fmt):
         assert d() == -7
 
 
+def test_append_decode_rejects_bad_arguments():
+    """The fused entry point: the decode's checks, plus its new rows and
+    slots (present, 16- and 4-byte aligned); nothing is launched."""
+    import sparse_mla_decode_amd as smla
+
+    def ad(rows=FAKE, slots=FAKE, **kw):
+        a = dict(q=FAKE, cache=FAKE, num_pages=10, page_table=FAKE, max_pages=4, seq_lens=FAKE,
+                 topk_indices=FAKE, batch=2, heads=16, topk=64, scale=0.04, out=FAKE, lse=FAKE,
+                 ws=FAKE, ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return smla.lib.smla_append_decode(
+            rows, slots, a["q"], a["cache"], a["num_pages"], a["page_table"], a["max_pages"],
+            a["seq_lens"], a["topk_indices"], a["batch"], a["heads"], a["topk"], a["scale"],
+            a["out"], a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+    assert ad(rows=None) == -1
+    assert ad(slots=None) == -1
+    assert ad(rows=FAKE + 8) == -4
+    assert ad(slots=FAKE + 2) == -4
+    assert ad(heads=32) == -3
+    assert ad(topk=0) == -2
+    assert ad(q=None) == -1
+    assert ad(cache=FAKE + 16) == -4
+    assert ad(batch=1, heads=64, topk=2048, ws=None, ws_bytes=0) == -5
+    import torch
+    if not torch.cuda.is_available():
+        assert ad() == -7
+
+
 def _append(fmt="", **kw):
     import sparse_mla_decode_amd as smla
     a = dict(rows=FAKE, n=5, slots=FAKE, cache=FAKE, num_pages=3, stream=None)
