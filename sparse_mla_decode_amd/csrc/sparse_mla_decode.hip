@@ -566,11 +566,17 @@ void sparse_mla_decode_kernel(const uint16_t *__restrict__ q, uint8_t *__restric
             const int pb = s & 1;
             write_weights(pb, d);
             if constexpr (!kFp8) {
-                // zero scales for the last tile's padding rows (see the value waves)
-                const bool real = (s + 1) * kTile <= n_valid || s * kTile + row < n_valid;
+                // zero scales for the last tile's padding rows (see the value
+                // waves); every other tile is full (a uniform branch)
+                if ((s + 1) * kTile <= n_valid) {
 #pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    st_lds[pb][(8 * g + k) * kSStride + row] = real ? sp[k][0] : (_Float16)0.0f;
+                    for (int k = 0; k < 8; ++k) st_lds[pb][(8 * g + k) * kSStride + row] = sp[k][0];
+                } else {
+                    const bool real = s * kTile + row < n_valid;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        st_lds[pb][(8 * g + k) * kSStride + row] = real ? sp[k][0] : (_Float16)0.0f;
+                }
             }
             bool over = false;
 #pragma unroll
